@@ -1,0 +1,231 @@
+#!/usr/bin/env python
+"""Throughput of the fused attention hot path on one MI355X.
+
+One step is the whole path once: the forward kernel (O, LSE), then the three
+backward stages (row pass, key-block pass, dQ conversion), on causal
+attention with B=4, H=16, N=4096, d=128 in bf16 (the forward+backward
+workload; Q, K, V, dO i.i.d. N(0, 1) from a fixed seed, already resident in
+HBM before timing starts).
+
+Work convention: forward 4*B*H*N^2*d flop, halved for causal; backward 2.5x
+the forward.  ``value`` is (forward + backward flop) / wall time per step, in
+TFLOP/s.  Per-kernel times come from HIP events recorded on the stream the
+kernels run on (torch's current stream, which the binding passes to the
+library), and the dominant kernel's roofline uses the chip's published dense
+bf16 MFMA peak of 2.5 PFLOP/s.
+
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+step (32 whole heads of 64, forward + backward) on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["fa_common.h", "fa_launch.h", "fa_fwd.hip", "fa_bwd.hip"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", help="named workload (default c5: fwd+bwd)")
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads of the step the CPU oracle times (0 = skip cpu_baseline)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_flash_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when there are none or the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
+
+
+def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
+    """The fp64 oracle on ``n_heads`` whole heads of the step, timed here."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(int(p.get("num_threads", 1)) for p in threadpool_info()
+                    if p.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    heads = [(0, 0), (wl.B - 1, wl.H - 1), (wl.B // 2, wl.H // 2), (0, wl.H - 1)][:n_heads]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention_forward(x["q"][sl], x["k"][sl], x["v"][sl], wl.scale, causal)
+        oracle.attention_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], wl.scale, causal)
+    dt = time.perf_counter() - t0
+    per_head = (wl.flops_fwd(causal) + wl.flops_bwd(causal)) / (wl.B * wl.H)
+    return {
+        "value": round(len(heads) * per_head / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"{len(heads)} of {wl.B * wl.H} heads of one step (forward + backward, "
+                   f"N={wl.N}, d={wl.d}, causal), float64 numpy, {dt:.2f} s; "
+                   f"same flop convention as value"),
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus N > 1 is not supported "
+              "(the path shards over (batch, head) with no exchange between GPUs)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    from exact_attention_flash_amd import binding as fa
+    from exact_attention_flash_amd.inputs import WORKLOADS, make_inputs
+
+    fa.load_library()  # fails loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    causal = wl.causal[-1]
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    scale = wl.scale
+    x = make_inputs(B, H, N, d, seed=wl.seed, with_dout=True)
+
+    import numpy as np
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda().contiguous()
+
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.flash_attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.flash_attn_fwd(q, k, v, causal=causal, softmax_scale=scale, out=o, lse=lse)
+        if evs:
+            evs[1].record(stream)
+        fa.flash_attn_bwd_preprocess(do, o, lse, ws)
+        if evs:
+            evs[2].record(stream)
+        fa.flash_attn_bwd_kv_blocks(do, q, k, v, dk, dv, ws, causal=causal, softmax_scale=scale)
+        if evs:
+            evs[3].record(stream)
+        fa.flash_attn_bwd_convert_dq(ws, dq, softmax_scale=scale)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_main", "fa_bwd_dq"]
+    avg_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps
+              for j, n in enumerate(names)}
+    rows = B * H * N
+    f_fwd, f_bwd = wl.flops_fwd(causal), wl.flops_bwd(causal)
+    work = {  # (bound, algorithmic work per launch, unit)
+        "fa_fwd": ("mfma", f_fwd),
+        "fa_bwd_pre": ("hbm", rows * d * 2 * 2 + rows * 4 + rows * d * 4 + rows * 4 * 2),
+        "fa_bwd_main": ("mfma", f_bwd),
+        "fa_bwd_dq": ("hbm", rows * d * 4 + rows * d * 2),
+    }
+    kernels = {}
+    for n in names:
+        bound, w = work[n]
+        t = avg_ms[n] * 1e-3
+        ach = w / t / (1e12 if bound == "mfma" else 1e9)
+        kernels[n] = {"avg_ms": round(avg_ms[n], 4), "bound": bound,
+                      "achieved": round(ach, 2), "unit": "TFLOP/s" if bound == "mfma" else "GB/s"}
+    dom = max(names, key=lambda n: avg_ms[n])
+    bound, w = work[dom]
+    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    achieved = w / (avg_ms[dom] * 1e-3) / (1e12 if bound == "mfma" else 1e9)
+    roofline = {
+        "bound": bound,
+        "kernel": dom,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": load_traffic(dom, kernel_source_sha()),
+        "work_per_launch": w,
+    }
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = f_fwd / (avg_ms["fa_fwd"] * 1e-3) / 1e12
+    bwd_ms = avg_ms["fa_bwd_pre"] + avg_ms["fa_bwd_main"] + avg_ms["fa_bwd_dq"]
+    line = {
+        "metric": "attention TFLOP/s (fwd+bwd) at 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{'causal' if causal else 'full'} attention fwd+bwd "
+                               f"B={B} H={H} N={N} d={d}",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if args.cpu_heads > 0:
+        line["cpu_baseline"] = cpu_baseline(x, wl, causal, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

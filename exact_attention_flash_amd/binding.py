@@ -1,0 +1,207 @@
+"""Thin ctypes binding over the C ABI in ``include/flash_attn.h``.
+
+Argument marshalling only: tensors are checked (bf16, contiguous, one device,
+``[B, H, N, d]``), outputs are allocated with torch when not given, and the
+raw device pointers plus the current HIP stream go to the library.  Every
+step of the computation runs in the HIP kernels; there is no other path.  If
+the shared library is missing the first call raises ``RuntimeError``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libexact_attention_flash_amd.so")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FlashAttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"flash_attn status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the HIP library, with argument types set."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"HIP library {p} is not built; run exact_attention_flash_amd.build.build()")
+        lib = ctypes.CDLL(p)
+        i64, vp, fl, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        lib.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, fl, vp]
+        lib.flash_attn_fwd.restype = ci
+        lib.flash_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.flash_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                       i64, i64, i64, i64, ci, fl, vp]
+        lib.flash_attn_bwd.restype = ci
+        lib.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, ctypes.c_size_t,
+                                                  i64, i64, i64, i64, vp]
+        lib.flash_attn_bwd_preprocess.restype = ci
+        lib.flash_attn_bwd_kv_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                 i64, i64, i64, i64, ci, fl, vp]
+        lib.flash_attn_bwd_kv_blocks.restype = ci
+        lib.flash_attn_bwd_convert_dq.argtypes = [vp, ctypes.c_size_t, vp, i64, i64, i64, i64,
+                                                  fl, vp]
+        lib.flash_attn_bwd_convert_dq.restype = ci
+        lib.flash_attn_status_string.argtypes = [ci]
+        lib.flash_attn_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def flash_attn_status_string(status: int) -> str:
+    return load_library().flash_attn_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FlashAttnError(status, flash_attn_status_string(status))
+
+
+def _check_tensors(*ts: torch.Tensor, names: str) -> tuple:
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError(f"{names.split(',')[0]} must be [B, H, N, d]")
+    for t, n in zip(ts, names.split(",")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        if t.device != ref.device or t.device.type != "cuda":
+            raise ValueError(f"{n} must be on the GPU device of {names.split(',')[0]}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    return tuple(ref.shape)
+
+
+def _stream_ptr(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def default_scale(d: int) -> float:
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def flash_attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().flash_attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                   softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, stream=None):
+    """O and LSE of softmax(scale * Q K^T) V; returns ``(out, lse)``."""
+    B, H, N, d = _check_tensors(q, k, v, names="q,k,v")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out, names="q,out")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, int(bool(causal)), scale,
+                                _stream_ptr(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   out: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+                   softmax_scale: float | None = None, dq: torch.Tensor | None = None,
+                   dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None):
+    """dQ, dK, dV of the attention whose forward gave ``out`` and ``lse``."""
+    B, H, N, d = _check_tensors(q, k, v, out, dout, names="q,k,v,out,dout")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensors(q, dq, dk, dv, names="q,dq,dk,dv")
+    lib = load_library()
+    need = int(lib.flash_attn_bwd_workspace_bytes(B, H, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
+                                int(bool(causal)), scale, _stream_ptr(q.device, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def _ws(workspace: torch.Tensor, device) -> tuple:
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def flash_attn_bwd_preprocess(dout: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                              workspace: torch.Tensor, stream=None) -> None:
+    """Stage 1 of the backward pass (row pass into the workspace)."""
+    B, H, N, d = _check_tensors(out, dout, names="out,dout")
+    wp, wb = _ws(workspace, out.device)
+    with torch.cuda.device(out.device):
+        st = load_library().flash_attn_bwd_preprocess(
+            out.data_ptr(), lse.data_ptr(), dout.data_ptr(), wp, wb, B, H, N, d,
+            _stream_ptr(out.device, stream))
+    _check(st)
+
+
+def flash_attn_bwd_kv_blocks(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                             v: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                             workspace: torch.Tensor, causal: bool = False,
+                             softmax_scale: float | None = None, stream=None) -> None:
+    """Stage 2 of the backward pass (key-block pass: dK, dV, dQ accumulator)."""
+    B, H, N, d = _check_tensors(q, k, v, dout, dk, dv, names="q,k,v,dout,dk,dv")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    wp, wb = _ws(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = load_library().flash_attn_bwd_kv_blocks(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dk.data_ptr(),
+            dv.data_ptr(), wp, wb, B, H, N, d, int(bool(causal)), scale,
+            _stream_ptr(q.device, stream))
+    _check(st)
+
+
+def flash_attn_bwd_convert_dq(workspace: torch.Tensor, dq: torch.Tensor,
+                              softmax_scale: float | None = None, stream=None) -> None:
+    """Stage 3 of the backward pass (dQ accumulator to bf16)."""
+    B, H, N, d = _check_tensors(dq, names="dq")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    wp, wb = _ws(workspace, dq.device)
+    with torch.cuda.device(dq.device):
+        st = load_library().flash_attn_bwd_convert_dq(wp, wb, dq.data_ptr(), B, H, N, d, scale,
+                                                      _stream_ptr(dq.device, stream))
+    _check(st)

@@ -1,0 +1,248 @@
+// C ABI of the fused attention library: argument validation and dispatch.
+// Every check runs on the host before any HIP call, so a rejected call has
+// no side effect.  The entry points are declared (with their contracts) in
+// include/flash_attn.h.
+#include "flash_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // keeps every byte count in int64
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape check shared by both passes.  Sets *empty for B*H*N == 0.
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) return FA_OK;
+  // sizes must fit the kernels' index arithmetic: N and B*H in int32, the
+  // element count well inside int64
+  if (N > INT32_MAX / 2 || B > INT32_MAX || H > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if (N > kMaxElems / d || bh > kMaxElems / (N * d)) return FA_ERR_BAD_SHAPE;
+  // grid sizes: query blocks of 64 rows (smallest tile) times heads must fit
+  // a one-dimensional launch
+  if (((N + 63) / 64) * bh > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float s) {
+  if (!std::isfinite(s) || !(s > 0.f)) return FA_ERR_BAD_SCALE;
+  return FA_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// True if any output range overlaps an input range or another output range.
+bool any_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+size_t ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const size_t rows = size_t(B) * size_t(H) * size_t(N);
+  return round_up(rows * size_t(d) * 4, kWsAlign) + 2 * round_up(rows * 4, kWsAlign);
+}
+
+// Pointers of the backward pass; `used` selects the ones a stage reads or
+// writes (the others may be null and are ignored).
+struct BwdPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* ws;
+};
+
+enum : unsigned {
+  kQ = 1u << 0, kK = 1u << 1, kV = 1u << 2, kO = 1u << 3, kLse = 1u << 4, kDout = 1u << 5,
+  kDq = 1u << 6, kDk = 1u << 7, kDv = 1u << 8, kWs = 1u << 9,
+  kAllBwd = (1u << 10) - 1
+};
+
+// Validate the arguments of a backward stage and fill its kernel arguments.
+// Returns FA_OK with a->BH == 0 for an empty problem.
+int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t B, int64_t H,
+                int64_t N, int64_t d, float scale, fa::BwdArgs* a) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  a->BH = 0;
+  if (empty) return FA_OK;
+  const void* ptrs[10] = {p.q, p.k, p.v, p.o, p.lse, p.dout, p.dq, p.dk, p.dv, p.ws};
+  for (int i = 0; i < 10; ++i)
+    if ((used >> i & 1u) && !ptrs[i]) return FA_ERR_NULL_POINTER;
+  for (int i = 0; i < 10; ++i)
+    if ((used >> i & 1u) && !aligned(ptrs[i], i == 4 ? 4 : 16)) return FA_ERR_MISALIGNED;
+  const size_t need = ws_bytes(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tb = size_t(B * H * N * d) * 2, lb = size_t(B * H * N) * 4;
+  Range ins[6], outs[4];
+  int n_in = 0, n_out = 0;
+  const size_t sizes[10] = {tb, tb, tb, tb, lb, tb, tb, tb, tb, need};
+  for (int i = 0; i < 10; ++i) {
+    if (!(used >> i & 1u)) continue;
+    if (i < 6) ins[n_in++] = range_of(ptrs[i], sizes[i]);
+    else outs[n_out++] = range_of(ptrs[i], sizes[i]);
+  }
+  if (any_alias(outs, n_out, ins, n_in)) return FA_ERR_ALIASING;
+
+  const size_t rows = size_t(B * H * N);
+  char* ws = static_cast<char*>(p.ws);
+  a->q = static_cast<const uint16_t*>(p.q);
+  a->k = static_cast<const uint16_t*>(p.k);
+  a->v = static_cast<const uint16_t*>(p.v);
+  a->o = static_cast<const uint16_t*>(p.o);
+  a->lse = p.lse;
+  a->dout = static_cast<const uint16_t*>(p.dout);
+  a->dq = static_cast<uint16_t*>(p.dq);
+  a->dk = static_cast<uint16_t*>(p.dk);
+  a->dv = static_cast<uint16_t*>(p.dv);
+  a->dq_acc = reinterpret_cast<float*>(ws);
+  a->delta = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign));
+  a->lse2 = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign) +
+                                     round_up(rows * 4, kWsAlign));
+  a->N = int(N);
+  a->BH = int(B * H);
+  a->scale = scale;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                   int64_t H, int64_t N, int64_t d, int causal, float softmax_scale, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_MISALIGNED;
+  const size_t tb = size_t(B * H * N * d) * 2, lb = size_t(B * H * N) * 4;
+  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range outs[2] = {range_of(o, tb), range_of(lse, lb)};
+  if (any_alias(outs, 2, ins, 3)) return FA_ERR_ALIASING;
+
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = int(N);
+  a.BH = int(B * H);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_fwd(a, int(d), causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, &empty) != FA_OK || empty) return 0;
+  return ws_bytes(B, H, N, d);
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                   float softmax_scale, void* stream) {
+  const BwdPtrs p{q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  fa::BwdArgs a;
+  const int st = prepare_bwd(p, kAllBwd, workspace_bytes, B, H, N, d, softmax_scale, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fa::launch_bwd_pre(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_main(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout, void* workspace,
+                              size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                              void* stream) {
+  const BwdPtrs p{nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace};
+  fa::BwdArgs a;
+  const int st = prepare_bwd(p, kO | kLse | kDout | kWs, workspace_bytes, B, H, N, d, 1.f, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  return fa::launch_bwd_pre(a, int(d), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FA_OK : FA_ERR_HIP;
+}
+
+int flash_attn_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                             float softmax_scale, void* stream) {
+  const BwdPtrs p{q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, workspace};
+  fa::BwdArgs a;
+  const int st = prepare_bwd(p, kQ | kK | kV | kDout | kDk | kDv | kWs, workspace_bytes, B, H, N,
+                             d, softmax_scale, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  return fa::launch_bwd_main(a, int(d), causal != 0, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int flash_attn_bwd_convert_dq(void* workspace, size_t workspace_bytes, void* dq, int64_t B,
+                              int64_t H, int64_t N, int64_t d, float softmax_scale,
+                              void* stream) {
+  const BwdPtrs p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr, nullptr,
+                  workspace};
+  fa::BwdArgs a;
+  const int st = prepare_bwd(p, kDq | kWs, workspace_bytes, B, H, N, d, softmax_scale, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  return fa::launch_bwd_dq(a, int(d), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FA_OK : FA_ERR_HIP;
+}
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 0 and the sizes must fit";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dim: d must be 64 or 128";
+    case FA_ERR_MISALIGNED: return "misaligned pointer: tensors need 16 bytes, LSE 4 bytes";
+    case FA_ERR_BAD_SCALE: return "softmax_scale must be finite and > 0";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flash_attn_bwd_workspace_bytes()";
+    case FA_ERR_ALIASING: return "an output buffer overlaps an input or another output";
+    case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

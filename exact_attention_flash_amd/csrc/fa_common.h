@@ -1,0 +1,171 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// vector types, the gfx950 bf16 MFMA, bf16 packing and small cross-lane ops.
+//
+// MFMA 32x32x16 (v_mfma_f32_32x32x16_bf16) register layout, for a wave of 64
+// lanes, lane = 32 * g + c with c in [0, 32) and g in {0, 1}:
+//   A (32 x 16, row-major view): lane holds A[c][8g .. 8g+7]
+//   B (16 x 32):                 lane holds B[8g .. 8g+7][c]
+//   C (32 x 32, fp32):           lane holds C[8(i/4) + 4g + i%4][c], i < 16
+// so a lane owns one output column and 16 of its rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 has a native converter).
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// 2^x on the transcendental unit; exact 0 for -inf.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2 on the transcendental unit, for positive normal inputs.
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of lane (lane ^ 32): swaps the two 32-lane halves of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+template <typename T>
+__device__ __forceinline__ T load_global(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+}  // namespace fa
+
+namespace fa {
+
+// Row order used for tiles that feed the A operand of a 32x32 MFMA whose C
+// rows must come out in runs of eight consecutive indices per lane: storing
+// row r at LDS row swap23(r) (bits 2 and 3 exchanged, an involution) makes
+// C value i of lane half g hold row 16 * (i / 8) + 8 * g + i % 8.
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Select the low (hi == 0) or high 16-bit halves of two words into one word:
+// result = { a.half, b.half }.
+__device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int hi) {
+  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+// ROWS x D bf16 tile of a row-major [N, D] matrix, staged global -> registers
+// -> LDS without transposition.  Rows at or beyond N read as zero.  LDS row
+// r holds source row swap23(r) when PERMUTE is set.
+template <int ROWS, int D, int NT, bool PERMUTE>
+struct RowTile {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int TASKS = ROWS * CPR;
+  static constexpr int PER = (TASKS + NT - 1) / NT;
+  u32x4 r[PER];
+
+  __device__ __forceinline__ void load(const uint16_t* base, int r0, int N, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = p * NT + tid;
+      const int row = t / CPR, ch = t % CPR;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (t < TASKS && r0 + row < N)
+        z = load_global<u32x4>(base + (int64_t)(r0 + row) * D + ch * 8);
+      r[p] = z;
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int pitch, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = p * NT + tid;
+      if (t < TASKS) {
+        const int row = t / CPR, ch = t % CPR;
+        const int lr = PERMUTE ? swap23(row) : row;
+        *reinterpret_cast<u32x4*>(lds + lr * pitch + ch * 8) = r[p];
+      }
+    }
+  }
+};
+
+// ROWS x D bf16 tile stored transposed in LDS ([D][ROWS], row pitch `pitch`
+// elements).  Each task owns four consecutive source rows of one 8-column
+// chunk and writes eight 8-byte runs (four rows of one column each).
+template <int ROWS, int D, int NT>
+struct TransTile {
+  static constexpr int GROUPS = ROWS / 4;
+  static constexpr int TASKS = GROUPS * (D / 8);
+  static constexpr int PER = (TASKS + NT - 1) / NT;
+  u32x4 r[PER][4];
+
+  __device__ __forceinline__ void load(const uint16_t* base, int r0, int N, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = p * NT + tid;
+      const int kg = t % GROUPS, ch = t / GROUPS;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = r0 + 4 * kg + u;
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (t < TASKS && row < N) z = load_global<u32x4>(base + (int64_t)row * D + ch * 8);
+        r[p][u] = z;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int pitch, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = p * NT + tid;
+      if (t < TASKS) {
+        const int kg = t % GROUPS, ch = t / GROUPS;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1, hi = e & 1;
+          u32x2 val;
+          val.x = pick_halves(r[p][0][w], r[p][1][w], hi);
+          val.y = pick_halves(r[p][2][w], r[p][3][w], hi);
+          *reinterpret_cast<u32x2*>(lds + (ch * 8 + e) * pitch + 4 * kg) = val;
+        }
+      }
+    }
+  }
+};
+
+}  // namespace fa

@@ -1,0 +1,212 @@
+// Fused attention forward for gfx950: O = softmax(scale * Q K^T) V and LSE.
+//
+// Method: the FlashAttention-2 forward outlined in the CMU 15-442/642 notes
+// "Transformer、注意力机制与优化" (section "FlashAttention-2 算法"): Q is cut
+// into row blocks, one per workgroup; K and V are streamed block by block
+// through on-chip memory; a running row max m, row sum l and unnormalised
+// output are updated with the notes' two-block merge (section
+// "安全 Softmax 与在线 Softmax"); O is divided by l once at the end and only
+// LSE = m + ln l is stored ("FlashAttention 系列技术详解", section
+// "具体优化策略").  Work is split over (batch, head, query block) and, inside
+// a workgroup, over query rows per wave, so no two waves ever combine partial
+// results (CMU notes, section "并行化策略").
+//
+// gfx950 mapping (one workgroup = 4 waves = 128 query rows; K/V tiles of 64
+// keys):
+//  * each wave computes S^T = K Q^T for its 32 queries with
+//    v_mfma_f32_32x32x16_bf16, so a lane owns one query and 32 of the tile's
+//    keys: the row max is an in-lane max plus one swap of wave halves, and
+//    the row sum needs no cross-lane step until the end;
+//  * K rows sit in LDS in swap23 order, which makes each lane's 16 scores per
+//    32-key block come out as two runs of eight consecutive keys: after
+//    rounding to bf16 they are directly the B operand of O^T += V^T P^T;
+//  * V is staged transposed (V^T, keys contiguous) so the A operand of the
+//    P V product is one 16-byte LDS read per MFMA;
+//  * exponentials are base 2 with log2(e) folded into the scale;
+//  * causal: key tiles past the block's last query are never loaded, tiles
+//    past a wave's last query are skipped by that wave, and only tiles that
+//    straddle the diagonal (or the ragged end of the sequence) are masked.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NT = NW * 64;       // threads per workgroup
+  static constexpr int QW = 32;            // query rows per wave
+  static constexpr int BR = NW * QW;       // query rows per workgroup
+  static constexpr int BC = 64;            // keys per K/V tile
+  static constexpr int KP = D + 8;         // K tile row pitch (elements)
+  static constexpr int VP = BC + 8;        // V^T tile row pitch (elements)
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr int BC = C::BC, KP = C::KP, VP = C::VP;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, g = lane >> 5;
+  const int N = a.N;
+  const int nqb = (N + C::BR - 1) / C::BR;
+
+  // Workgroup -> (head, query block).  Consecutive workgroup ids land on
+  // different XCDs (round robin over 8); give each XCD a contiguous run of
+  // work so the query blocks of one head share that XCD's L2.  Within a head
+  // the heaviest (last) causal blocks go first.
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int bh = L / nqb;
+  int qb = L - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+
+  const int64_t hoff = (int64_t)bh * N * D;
+  const uint16_t* Qh = a.q + hoff;
+  const uint16_t* Kh = a.k + hoff;
+  const uint16_t* Vh = a.v + hoff;
+  const int q0 = qb * C::BR;
+  const int qw0 = q0 + w * C::QW;
+  const int qrow = qw0 + c32;  // the query this lane owns
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc)
+    qf[kc] = qrow < N ? load_global<bf16x8>(Qh + (int64_t)qrow * D + kc * 16 + g * 8)
+                      : zero_bf16x8();
+
+  int nt = (N + BC - 1) / BC;
+  if (CAUSAL) nt = min(nt, (q0 + C::BR + BC - 1) / BC);
+
+  RowTile<BC, D, C::NT, true> kt;
+  TransTile<BC, D, C::NT> vt;
+
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s for this query
+  float l_part = 0.f;       // this lane's share of the running row sum
+  f32x16 oacc[D / 32];      // O^T block: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+
+  const float sl2 = a.scale_log2;
+
+  kt.load(Kh, 0, N, tid);
+  vt.load(Vh, 0, N, tid);
+  for (int j = 0; j < nt; ++j) {
+    kt.store(Ks, KP, tid);
+    vt.store(Vt, VP, tid);
+    __syncthreads();
+    if (j + 1 < nt) {
+      kt.load(Kh, (j + 1) * BC, N, tid);
+      vt.load(Vh, (j + 1) * BC, N, tid);
+    }
+    const int k0 = j * BC;
+    const bool skip = CAUSAL && (k0 > qw0 + C::QW - 1);
+    if (!skip) {
+      // S^T for the tile: two 32-key blocks.  Value i of s[sb] is the score
+      // of key k0 + 32 sb + 16 (i / 8) + 8 g + i % 8 against qrow.
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb) {
+        s[sb] = zero16();
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(Ks + (sb * 32 + c32) * KP + kc * 16 + g * 8);
+          s[sb] = mfma32(ka, qf[kc], s[sb]);
+        }
+      }
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
+      if (need_mask) {
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * sb + 16 * (i >> 3) + 8 * g + (i & 7);
+            if (key >= N || (CAUSAL && key > qrow)) s[sb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      // A query with every key so far masked keeps m = -inf; shift by 0 then
+      // so that no (-inf) - (-inf) is formed.
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(fmaf(s[sb][i], sl2, -m_use));
+          s[sb][i] = p;
+          rs += p;
+        }
+      l_part = fmaf(l_part, alpha, rs);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      // P^T as bf16 B operands: chunk kc2 covers keys k0 + 16 kc2 + 8 g + 0..7.
+      bf16x8 pb[BC / 16];
+#pragma unroll
+      for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
+        float t[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) t[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
+        pb[kc2] = pack8(t);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
+          const bf16x8 va =
+              *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + c32) * VP + kc2 * 16 + g * 8);
+          oacc[db] = mfma32(va, pb[kc2], oacc[db]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
+  const float l = l_part + swap_halves(l_part);
+  if (qrow < N) {
+    const float inv = 1.f / l;
+    uint16_t* Orow = a.o + hoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 val;
+        val.x = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+        val.y = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * g) = val;
+      }
+    if (g == 0) a.lse[(int64_t)bh * N + qrow] = (m_run + log2_fast(l)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int64_t nqb = (a.N + C::BR - 1) / C::BR;
+  const int64_t grid = nqb * a.BH;
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
+  return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,50 @@
+// Kernel argument blocks and launchers, shared by the C ABI layer (api.cpp)
+// and the kernel translation units.  Plain data only: the ABI layer has
+// already validated every field when these are filled.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;  // bf16 [B, H, N, d]
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;        // bf16 [B, H, N, d]
+  float* lse;         // fp32 [B, H, N], natural log
+  int N;              // sequence length
+  int BH;             // B * H
+  float scale_log2;   // softmax_scale * log2(e), > 0
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;      // workspace: fp32 [B, H, N, d]
+  float* delta;       // workspace: fp32 [B, H, N], rowsum(dO o O)
+  float* lse2;        // workspace: fp32 [B, H, N], LSE * log2(e)
+  int N;
+  int BH;
+  float scale;        // softmax_scale, > 0
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Enqueue the forward kernel for head dim d (64 or 128).
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// The three backward stages, each one kernel launch, for head dim d (64 or
+// 128): the row pass, the pass over key blocks, and the dQ conversion.
+hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,156 @@
+/*
+ * flash_attn.h - C ABI of the fused exact-attention library for AMD MI355X
+ * (gfx950).
+ *
+ * What is computed (sources are the web pages the method is described on):
+ *
+ *   O = softmax(scale * Q K^T) V          per (batch, head)
+ *
+ * the scaled dot-product attention of "优化的注意力实现 (FlashAttention)"
+ * (apxml course page, section "标准注意力中的内存带宽瓶颈") and of the CMU
+ * 15-442/642 notes "Transformer、注意力机制与优化" (section "数学公式"), with
+ * Q, K, V in R^{N x d}.  The forward pass is one fused, tiled kernel that
+ * keeps a running row maximum m and row sum l (same notes, section
+ * "安全 Softmax 与在线 Softmax") so the N x N score matrix never reaches
+ * device memory; it stores O and, per row, LSE = m + ln l, the single
+ * statistic the FlashAttention-2 forward keeps for the backward pass
+ * ("FlashAttention 系列技术详解", section "具体优化策略").  The backward pass
+ * recomputes the scores from LSE ("FlashAttention 的基本原理", section 2.4)
+ * and accumulates dQ across key blocks with atomic adds in device memory
+ * (CMU notes, section "为什么前向和反向的并行化策略不同").
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major [B, H, N, d]: element (b, h, n, c) is at
+ *    ((b * H + h) * N + n) * d + c.  Q, K, V, O, dO, dQ, dK, dV are bf16
+ *    (passed as raw pointers to 16-bit storage); LSE is float32 [B, H, N].
+ *  - Queries and keys have the same length N.  Causal masking lets query i
+ *    see key j iff j <= i (the apxml example's tril(diagonal=0) mask).
+ *  - softmax_scale multiplies Q K^T before masking and softmax; it must be
+ *    finite and > 0 (the pages' scale is 1/sqrt(d)).
+ *  - LSE is the natural-log log-sum-exp of the scaled, masked scores.
+ *  - Supported head dims: d = 64 and d = 128.  Any N >= 1 (ragged tails are
+ *    masked).  B, H >= 1.  B = 0, H = 0 or N = 0 is an empty problem: the
+ *    call returns FA_OK at once and touches no pointer.
+ *  - Every device pointer must be 16-byte aligned (LSE: 4-byte).
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    backward workspace.  The library never allocates, frees or keeps device
+ *    memory and holds no mutable global state; calls on different streams
+ *    may run concurrently.
+ *  - Outputs are fully overwritten and must not overlap any input or each
+ *    other (FA_ERR_ALIASING).
+ *  - Errors: arguments are validated synchronously, before any HIP call, and
+ *    an error leaves every buffer untouched.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the null stream) and runs asynchronously;
+ *    FA_ERR_HIP reports a failed launch (hipGetLastError after enqueueing).
+ *    Faults during execution surface at the caller's next synchronisation.
+ *  - There is no fallback path: an unsupported argument is an error.
+ */
+#ifndef FLASH_ATTN_MI355X_H
+#define FLASH_ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,           /* B, H or N negative, or sizes overflow */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3,/* d is not 64 or 128 */
+  FA_ERR_MISALIGNED = 4,          /* a pointer breaks the alignment rule */
+  FA_ERR_BAD_SCALE = 5,           /* softmax_scale is NaN, Inf or <= 0 */
+  FA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the required size */
+  FA_ERR_ALIASING = 7,            /* an output overlaps an input or output */
+  FA_ERR_HIP = 8                  /* the HIP runtime rejected a launch */
+};
+
+/*
+ * Forward pass.
+ *   q, k, v : in,  bf16 [B, H, N, d]
+ *   o       : out, bf16 [B, H, N, d]   O = softmax(scale * Q K^T (masked)) V
+ *   lse     : out, fp32 [B, H, N]      LSE = m + ln l of each query row
+ *   causal  : 0 = full attention, non-zero = causal mask
+ * Follows the FlashAttention-2 outline of the CMU notes (section
+ * "FlashAttention-2 算法"): one query block per workgroup, K/V blocks
+ * streamed through on-chip memory, running (m, l, O) in registers, one
+ * division by l at the end.  Deterministic: identical inputs give
+ * bit-identical O and LSE.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v,
+                   void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   int causal, float softmax_scale, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs for this shape: an fp32
+ * dQ accumulator [B, H, N, d] and two fp32 row vectors [B, H, N] (the
+ * rowsum(dO o O) term and LSE in base 2), each section rounded up to 256
+ * bytes.  Returns 0 for an empty problem and for invalid sizes.
+ */
+size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * Backward pass (recompute from LSE).
+ *   q, k, v, o : in, bf16 [B, H, N, d]  (o and lse from flash_attn_fwd with
+ *                the same q, k, v, causal and softmax_scale)
+ *   lse        : in, fp32 [B, H, N]
+ *   dout       : in, bf16 [B, H, N, d]  gradient of the loss w.r.t. O
+ *   dq, dk, dv : out, bf16 [B, H, N, d]
+ *   workspace  : device memory of at least
+ *                flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *                aligned, no initialisation needed, caller-owned; it must
+ *                not overlap any other argument.
+ * Three launches on `stream`: a row pass (D_i = sum_c dO_ic O_ic, LSE in
+ * base 2, dQ accumulator cleared), the main pass over key blocks (dK, dV
+ * in registers, dQ by fp32 atomic adds), and the dQ conversion to bf16.
+ * dQ's rounding depends on the order of the atomic adds, so it may differ
+ * in the last bits from run to run; dK and dV are deterministic.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   int causal, float softmax_scale, void* stream);
+
+/*
+ * The three stages of flash_attn_bwd as separate calls, one kernel launch
+ * each, for callers that want to time a stage or put other work between
+ * stages.  Enqueued in this order on one stream, with the same shapes and
+ * workspace, they are exactly flash_attn_bwd.  Each validates only the
+ * pointers it uses (the same rules as flash_attn_bwd); the workspace
+ * carries the state from one stage to the next.
+ *
+ * flash_attn_bwd_preprocess: D_i = sum_c dO_ic O_ic and LSE * log2(e) into
+ *   the workspace, dQ accumulator cleared.  Reads o, lse, dout.
+ * flash_attn_bwd_kv_blocks: the pass over key blocks.  Reads q, k, v, dout
+ *   and the workspace written by the preprocess stage; writes dk, dv and
+ *   adds into the workspace's dQ accumulator.
+ * flash_attn_bwd_convert_dq: dq = bf16(softmax_scale * dQ accumulator).
+ */
+int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout,
+                              void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
+int flash_attn_bwd_kv_blocks(const void* q, const void* k, const void* v,
+                             const void* dout, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             int64_t B, int64_t H, int64_t N, int64_t d,
+                             int causal, float softmax_scale, void* stream);
+
+int flash_attn_bwd_convert_dq(void* workspace, size_t workspace_bytes, void* dq,
+                              int64_t B, int64_t H, int64_t N, int64_t d,
+                              float softmax_scale, void* stream);
+
+/* Static, human-readable text for a status code ("unknown status" if none). */
+const char* flash_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_MI355X_H */

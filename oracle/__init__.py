@@ -34,6 +34,7 @@ from .attention import (
     softmax_row_grad,
     attention_probs,
     attention_forward,
+    attention_forward_rows,
     attention_backward,
 )
 from .online_softmax import (
@@ -50,6 +51,7 @@ __all__ = [
     "softmax_row_grad",
     "attention_probs",
     "attention_forward",
+    "attention_forward_rows",
     "attention_backward",
     "softmax_stats",
     "merge_stats",

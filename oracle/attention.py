@@ -52,8 +52,12 @@ def _f64(x) -> np.ndarray:
 
 # ---------------------------------------------------------------- forward
 def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-           row_start: int = 0) -> np.ndarray:
-    """S = scale * Q K^T for one head, rows ``row_start ..``, masked if causal.
+           row_start: int = 0, rows=None) -> np.ndarray:
+    """S = scale * Q K^T for one head, masked if causal.
+
+    ``q`` holds query rows ``row_start, row_start + 1, ...`` of the head, or,
+    when ``rows`` is given, the rows with those global indices (the mask
+    needs the global index of each query).
 
     Definition: apxml page, equation softmax(QK^T/sqrt(d_k))V and the manual
     fallback in its example (matmul, multiply by the scale factor, add the
@@ -62,9 +66,11 @@ def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
     """
     s = (q @ k.T) * np.float64(scale)
     if causal:
-        rows = np.arange(row_start, row_start + q.shape[0])[:, None]
+        if rows is None:
+            rows = np.arange(row_start, row_start + q.shape[0])
+        r = np.asarray(rows)[:, None]
         cols = np.arange(k.shape[0])[None, :]
-        s = np.where(cols > rows, -np.inf, s)
+        s = np.where(cols > r, -np.inf, s)
     return s
 
 
@@ -127,6 +133,20 @@ def attention_forward(q, k, v, scale: float, causal: bool,
                 O[b, h, r0:r0 + R] = p @ v[b, h]
                 LSE[b, h, r0:r0 + R] = m + np.log(ell)
     return O, LSE
+
+
+def attention_forward_rows(q, k, v, scale: float, causal: bool, rows):
+    """O and LSE of one head ``[N, d]`` for the query rows listed in ``rows``.
+
+    The same definition as ``attention_forward``: every listed row is
+    computed in full against all N keys; rows are independent, so this is
+    the whole-head result restricted to those rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scores(q[rows], k, scale, causal, rows=rows)
+    m, ell, p = softmax_rows(s)
+    return p @ v, m + np.log(ell)
 
 
 # ---------------------------------------------------------------- backward

@@ -1,0 +1,157 @@
+"""The C ABI library: it loads, exports every entry point the header declares,
+and rejects bad arguments on the host, before any HIP call.
+
+The rejection tests pass fake (never dereferenced) pointer values.  They run
+only in a process without a GPU, so that a validation bug could at worst get
+a launch error from a missing device, never a kernel touching fake memory.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from exact_attention_flash_amd.binding import LIB_PATH, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR = range(9)
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake-pointer validation runs only without a GPU")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(flash_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_header_symbols():
+    lib = load_library()
+    names = _declared()
+    assert names == sorted(["flash_attn_fwd", "flash_attn_bwd",
+                            "flash_attn_bwd_workspace_bytes", "flash_attn_status_string",
+                            "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
+                            "flash_attn_bwd_convert_dq"])
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (flash_attn_\w+)", out.stdout))
+        assert set(names) <= exported
+
+
+def test_status_strings():
+    lib = load_library()
+    for s in range(9):
+        assert lib.flash_attn_status_string(s) not in (None, b"unknown status")
+    assert lib.flash_attn_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    lib = load_library()
+    rows = 4 * 16 * 4096
+    want = (rows * 128 * 4 + 255) // 256 * 256 + 2 * ((rows * 4 + 255) // 256 * 256)
+    assert lib.flash_attn_bwd_workspace_bytes(4, 16, 4096, 128) == want
+    assert lib.flash_attn_bwd_workspace_bytes(1, 1, 1, 64) == 256 + 2 * 256
+    assert lib.flash_attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+    assert lib.flash_attn_bwd_workspace_bytes(1, 1, 10, 96) == 0
+    assert lib.flash_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
+
+
+A = 1 << 20  # fake, 16-byte-aligned addresses spaced far apart
+
+
+def _fwd(lib, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, N=16, d=64, causal=0,
+         scale=0.125):
+    return lib.flash_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@no_gpu
+def test_fwd_validation():
+    lib = load_library()
+    assert _fwd(lib, B=0) == FA_OK and _fwd(lib, N=0, q=None) == FA_OK  # empty: no-op
+    assert _fwd(lib, q=None) == NULLP
+    assert _fwd(lib, lse=None) == NULLP
+    assert _fwd(lib, N=-1) == SHAPE
+    assert _fwd(lib, B=1 << 40, N=1 << 20) == SHAPE
+    assert _fwd(lib, d=96) == HEADDIM and _fwd(lib, d=256) == HEADDIM
+    assert _fwd(lib, q=A + 8) == MISAL
+    assert _fwd(lib, lse=5 * A + 2) == MISAL
+    assert _fwd(lib, lse=5 * A + 4) != MISAL
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        assert _fwd(lib, scale=bad) == SCALE
+    assert _fwd(lib, o=A) == ALIAS                       # O on top of Q
+    assert _fwd(lib, lse=4 * A + 16) == ALIAS            # LSE inside O
+    assert _fwd(lib, o=A + 16 * 64 * 2) != ALIAS         # O just after Q
+
+
+def _bwd(lib, ws_bytes=None, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+                ws=10 * A, B=1, H=2, N=16, d=128, causal=1, scale=0.1)
+    args.update(kw)
+    need = lib.flash_attn_bwd_workspace_bytes(args["B"], args["H"], args["N"], args["d"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return lib.flash_attn_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"],
+                              args["dq"], args["dk"], args["dv"], args["ws"], wsb, args["B"],
+                              args["H"], args["N"], args["d"], args["causal"], args["scale"], None)
+
+
+@no_gpu
+def test_bwd_validation():
+    lib = load_library()
+    assert _bwd(lib, H=0, ws=None) == FA_OK
+    assert _bwd(lib, ws=None) == NULLP
+    assert _bwd(lib, do=None) == NULLP
+    assert _bwd(lib, d=32) == HEADDIM
+    assert _bwd(lib, dk=8 * A + 2) == MISAL
+    assert _bwd(lib, scale=float("-inf")) == SCALE
+    need = lib.flash_attn_bwd_workspace_bytes(1, 2, 16, 128)
+    assert _bwd(lib, ws_bytes=need - 1) == WS
+    assert _bwd(lib, dq=A) == ALIAS          # dQ on Q
+    assert _bwd(lib, dv=8 * A) == ALIAS      # dV on dK
+    assert _bwd(lib, ws=6 * A) == ALIAS      # workspace on dO
+
+
+@no_gpu
+def test_bwd_stage_validation():
+    lib = load_library()
+    need = lib.flash_attn_bwd_workspace_bytes(1, 2, 16, 128)
+    # stages check only the pointers they use
+    assert lib.flash_attn_bwd_preprocess(None, 5 * A, 6 * A, 10 * A, need, 1, 2, 16, 128,
+                                         None) == NULLP
+    assert lib.flash_attn_bwd_preprocess(4 * A, 5 * A, 6 * A, 10 * A, need - 4, 1, 2, 16, 128,
+                                         None) == WS
+    assert lib.flash_attn_bwd_preprocess(4 * A, 5 * A, 6 * A, 4 * A, need, 1, 2, 16, 128,
+                                         None) == ALIAS
+    assert lib.flash_attn_bwd_kv_blocks(A, 2 * A, 3 * A, 6 * A, 8 * A, 9 * A, 10 * A, need,
+                                        1, 2, 16, 96, 1, 0.1, None) == HEADDIM
+    assert lib.flash_attn_bwd_kv_blocks(A, 2 * A, 3 * A, 6 * A, 8 * A, 8 * A, 10 * A, need,
+                                        1, 2, 16, 128, 1, 0.1, None) == ALIAS
+    assert lib.flash_attn_bwd_kv_blocks(A, 2 * A, 3 * A, 6 * A, 8 * A, 9 * A, 10 * A, need,
+                                        1, 2, 16, 128, 1, 0.0, None) == SCALE
+    assert lib.flash_attn_bwd_convert_dq(10 * A, need, 7 * A + 4, 1, 2, 16, 128, 0.1,
+                                         None) == MISAL
+    assert lib.flash_attn_bwd_convert_dq(10 * A, need, 7 * A, 0, 2, 16, 128, 0.1, None) == FA_OK
+
+
+@no_gpu
+def test_valid_call_without_device_reports_hip_error():
+    """All arguments valid: the call reaches the launch, which fails with no
+    device present and is reported as FA_ERR_HIP (no fake memory is touched
+    because nothing can run)."""
+    lib = load_library()
+    assert _fwd(lib) == HIPERR
+
+
+def test_python_binding_rejects_cpu_tensors():
+    from exact_attention_flash_amd import flash_attn_fwd
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        flash_attn_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        flash_attn_fwd(q.float(), q.float(), q.float())

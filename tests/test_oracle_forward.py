@@ -186,3 +186,14 @@ def test_bf16_bits_are_widened_exactly():
     assert np.array_equal(O_bits, O_f)
     with pytest.raises(TypeError):
         oracle.widen_bf16(np.zeros(3, dtype=np.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_selected_rows_match_whole_head(causal):
+    N, d = 40, 8
+    q, k, v = _rand(1, 1, N, d), _rand(1, 1, N, d), _rand(1, 1, N, d)
+    O, L = oracle.attention_forward(q, k, v, 0.45, causal)
+    rows = np.array([0, 39, 7, 8, 20, 1])
+    Or, Lr = oracle.attention_forward_rows(q[0, 0], k[0, 0], v[0, 0], 0.45, causal, rows)
+    assert np.array_equal(Or, O[0, 0, rows]) or np.allclose(Or, O[0, 0, rows], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(Lr, L[0, 0, rows], rtol=1e-15, atol=1e-15)
