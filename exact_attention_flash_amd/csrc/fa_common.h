@@ -169,3 +169,61 @@ struct TransTile {
 };
 
 }  // namespace fa
+
+namespace fa {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
+
+// Asynchronous 16-byte copy global -> LDS.  Lane i of the wave writes its 16
+// bytes at lds_wave_base + 16 * i; lds_wave_base must be the same for every
+// lane of the wave.  Completion is tracked by the wave's vmcnt.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until every global load (including global -> LDS copies) of this wave
+// has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4e + q supplies the address of 4 consecutive 16-bit values;
+// lane i of the group receives element i % 4 of the run supplied by lane
+// 4e + i / 4, for e = 0..3.  With lane 4e + q pointing at M[r0 + e][c0 + 4q],
+// lane i receives M[r0 .. r0+3][c0 + i]: a column of four rows.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Two transposed reads joined into one bf16x8 MFMA operand (lo = elements
+// 0..3, hi = 4..7).  Joined as a 16-bit integer shuffle and bit-cast once:
+// inserting bit-cast bf16 elements one at a time is miscompiled by this
+// toolchain (the upper half of each read is dropped).
+__device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
+  const i16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// XOR swizzle of the 16-byte chunks of an unpadded row-major LDS tile, so
+// that the MFMA operand reads (16 rows at one chunk; 4 rows at 4 chunks for
+// the transposed reads) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 128) {
+    return ((row & 1) ? 0x6 : 0) ^ ((row & 2) ? 0xC : 0) ^ ((row & 4) ? 0x1 : 0) ^
+           ((row & 8) ? 0x8 : 0);
+  } else {
+    return ((row << 1) ^ (row >> 2)) & 7;
+  }
+}
+
+// Element offset of (row, col) in a swizzled [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ chunk_swizzle<D>(row))) << 3) + (col & 7);
+}
+
+}  // namespace fa

@@ -12,17 +12,25 @@
 // results (CMU notes, section "并行化策略").
 //
 // gfx950 mapping (one workgroup = 4 waves = 128 query rows; K/V tiles of 64
-// keys):
+// keys; two workgroups per CU):
+//  * K and V tiles go global -> LDS with asynchronous 16-byte copies
+//    (global_load_lds_dwordx4) into a double buffer: the next tile is in
+//    flight while the current one is used, and no register holds staging
+//    data.  Tiles are unpadded row-major with an XOR swizzle of the 16-byte
+//    chunks, so that operand reads are free of bank conflicts;
 //  * each wave computes S^T = K Q^T for its 32 queries with
 //    v_mfma_f32_32x32x16_bf16, so a lane owns one query and 32 of the tile's
-//    keys: the row max is an in-lane max plus one swap of wave halves, and
-//    the row sum needs no cross-lane step until the end;
+//    keys: the row max is an in-lane max plus one swap of wave halves, and the
+//    row sum needs no cross-lane step until the end;
 //  * K rows sit in LDS in swap23 order, which makes each lane's 16 scores per
-//    32-key block come out as two runs of eight consecutive keys: after
-//    rounding to bf16 they are directly the B operand of O^T += V^T P^T;
-//  * V is staged transposed (V^T, keys contiguous) so the A operand of the
-//    P V product is one 16-byte LDS read per MFMA;
-//  * exponentials are base 2 with log2(e) folded into the scale;
+//    32-key block come out as two runs of eight consecutive keys: rounded to
+//    bf16 they are directly the B operand of O^T += V^T P^T;
+//  * the V^T operand of that product is read from the row-major V tile with
+//    the transposing LDS read (ds_read_b64_tr_b16);
+//  * exponentials are base 2 with log2(e) folded into the scale, and the
+//    running max is only moved (and O, l rescaled) when a tile's max exceeds
+//    it by more than 2^8: until then the probabilities are taken relative to
+//    the stale max, which changes nothing after the final division by l;
 //  * causal: key tiles past the block's last query are never loaded, tiles
 //    past a wave's last query are skipped by that wave, and only tiles that
 //    straddle the diagonal (or the ragged end of the sequence) are masked.
@@ -33,21 +41,49 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = 4;             // waves per workgroup
-  static constexpr int NT = NW * 64;       // threads per workgroup
-  static constexpr int QW = 32;            // query rows per wave
-  static constexpr int BR = NW * QW;       // query rows per workgroup
-  static constexpr int BC = 64;            // keys per K/V tile
-  static constexpr int KP = D + 8;         // K tile row pitch (elements)
-  static constexpr int VP = BC + 8;        // V^T tile row pitch (elements)
+  static constexpr int NW = 4;                      // waves per workgroup
+  static constexpr int NT = NW * 64;                // threads per workgroup
+  static constexpr int QW = 32;                     // query rows per wave
+  static constexpr int BR = NW * QW;                // query rows per workgroup
+  static constexpr int BC = 64;                     // keys per K/V tile
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int TILE = BC * D;               // elements per K or V tile
+  static constexpr int COPIES = BC * CPR / NT;      // 16-byte copies per thread per tile
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
+// Largest growth of the probabilities (in log2 units) tolerated before the
+// running max is moved.
+constexpr float kRescaleThreshold = 8.f;
+
+// Issue the asynchronous copies of key tile [k0, k0 + BC) of K and V into
+// one LDS stage.  K row r of the tile holds key k0 + swap23(r); V row r holds
+// key k0 + r.  Rows past the end of the sequence copy the last valid row
+// (finite data; those keys are masked, so they contribute nothing).
+template <int D>
+__device__ __forceinline__ void issue_kv_tile(const uint16_t* Kh, const uint16_t* Vh,
+                                              uint16_t* Ks, uint16_t* Vs, int k0, int N,
+                                              int w, int lane) {
   using C = FwdCfg<D>;
-  constexpr int BC = C::BC, KP = C::KP, VP = C::VP;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+#pragma unroll
+  for (int t = 0; t < C::COPIES; ++t) {
+    const int slot = (t * C::NW + w) * 64 + lane;  // 16-byte slot in the tile
+    const int row = slot / C::CPR;
+    const int pc = slot % C::CPR;                  // physical chunk
+    const int lc = pc ^ chunk_swizzle<D>(row);     // logical chunk it holds
+    const int kk = min(k0 + swap23(row), N - 1);
+    const int vk = min(k0 + row, N - 1);
+    const int wave_base = (t * C::NW + w) * 64 * 8;  // elements
+    load_lds16(Kh + (int64_t)kk * D + lc * 8, Ks + wave_base);
+    load_lds16(Vh + (int64_t)vk * D + lc * 8, Vs + wave_base);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr int BC = C::BC, TILE = C::TILE;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, g = lane >> 5;
@@ -73,6 +109,11 @@ __global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
   const int qw0 = q0 + w * C::QW;
   const int qrow = qw0 + c32;  // the query this lane owns
 
+  int nt = (N + BC - 1) / BC;
+  if (CAUSAL) nt = min(nt, (q0 + C::BR + BC - 1) / BC);
+
+  issue_kv_tile<D>(Kh, Vh, smem, smem + TILE, 0, N, w, lane);
+
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -80,29 +121,24 @@ __global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
     qf[kc] = qrow < N ? load_global<bf16x8>(Qh + (int64_t)qrow * D + kc * 16 + g * 8)
                       : zero_bf16x8();
 
-  int nt = (N + BC - 1) / BC;
-  if (CAUSAL) nt = min(nt, (q0 + C::BR + BC - 1) / BC);
-
-  RowTile<BC, D, C::NT, true> kt;
-  TransTile<BC, D, C::NT> vt;
-
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s for this query
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s (possibly stale)
   float l_part = 0.f;       // this lane's share of the running row sum
   f32x16 oacc[D / 32];      // O^T block: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-
   const float sl2 = a.scale_log2;
 
-  kt.load(Kh, 0, N, tid);
-  vt.load(Vh, 0, N, tid);
+  // transposed-read lane roles (see lds_read_tr)
+  const int tr_g = lane >> 5, tr_e = (lane >> 2) & 3, tr_q = lane & 3, tr_half = (lane >> 4) & 1;
+
+  wait_vmem();
+  __syncthreads();
   for (int j = 0; j < nt; ++j) {
-    kt.store(Ks, KP, tid);
-    vt.store(Vt, VP, tid);
-    __syncthreads();
+    const uint16_t* Ks = smem + (j & 1) * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
     if (j + 1 < nt) {
-      kt.load(Kh, (j + 1) * BC, N, tid);
-      vt.load(Vh, (j + 1) * BC, N, tid);
+      uint16_t* nk = smem + ((j + 1) & 1) * 2 * TILE;
+      issue_kv_tile<D>(Kh, Vh, nk, nk + TILE, (j + 1) * BC, N, w, lane);
     }
     const int k0 = j * BC;
     const bool skip = CAUSAL && (k0 > qw0 + C::QW - 1);
@@ -111,15 +147,15 @@ __global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
       // of key k0 + 32 sb + 16 (i / 8) + 8 g + i % 8 against qrow.
       f32x16 s[BC / 32];
 #pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb) {
-        s[sb] = zero16();
+      for (int sb = 0; sb < BC / 32; ++sb) s[sb] = zero16();
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(Ks + (sb * 32 + c32) * KP + kc * 16 + g * 8);
+      for (int kc = 0; kc < D / 16; ++kc)
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb) {
+          const int row = sb * 32 + c32;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + swz_off<D>(row, kc * 16 + g * 8));
           s[sb] = mfma32(ka, qf[kc], s[sb]);
         }
-      }
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
       if (need_mask) {
 #pragma unroll
@@ -135,13 +171,21 @@ __global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      // A query with every key so far masked keeps m = -inf; shift by 0 then
-      // so that no (-inf) - (-inf) is formed.
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
+      mx = fmaxf(mx, swap_halves(mx)) * sl2;
+      // Move the running max only when some query's probabilities would grow
+      // past 2^threshold (always on the first visible tile, where m = -inf).
+      if (__ballot(mx > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mx);
+        // a query with every key so far masked keeps m = -inf and nothing to rescale
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
@@ -151,29 +195,27 @@ __global__ void __launch_bounds__(256) fa_fwd_kernel(FwdArgs a) {
           s[sb][i] = p;
           rs += p;
         }
-      l_part = fmaf(l_part, alpha, rs);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      // P^T as bf16 B operands: chunk kc2 covers keys k0 + 16 kc2 + 8 g + 0..7.
-      bf16x8 pb[BC / 16];
+      l_part += rs;
+      // O^T += V^T P^T over the tile's four 16-key chunks.  B operand: P^T
+      // chunk kc2 (keys k0 + 16 kc2 + 8 g + 0..7 of this lane's query).  A
+      // operand: V^T rows 32 db + c32, read transposed from the V tile.
 #pragma unroll
       for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
         float t[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) t[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
-        pb[kc2] = pack8(t);
-      }
+        const bf16x8 pb = pack8(t);
+        const int vrow = 16 * kc2 + 8 * tr_g + tr_e;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + c32) * VP + kc2 * 16 + g * 8);
-          oacc[db] = mfma32(va, pb[kc2], oacc[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int vcol = 32 * db + 16 * tr_half + 4 * tr_q;
+          const bf16x8 va = join_tr(lds_read_tr(Vs + swz_off<D>(vrow, vcol)),
+                                    lds_read_tr(Vs + swz_off<D>(vrow + 4, vcol)));
+          oacc[db] = mfma32(va, pb, oacc[db]);
         }
+      }
     }
+    wait_vmem();
     __syncthreads();
   }
 
