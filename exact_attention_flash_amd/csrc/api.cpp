@@ -65,9 +65,16 @@ bool any_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
   return false;
 }
 
+int64_t padded_rows(int64_t N) {
+  return (N + fa::kBwdQueryBlock - 1) / fa::kBwdQueryBlock * fa::kBwdQueryBlock;
+}
+
+// Workspace layout: fp32 dQ accumulator [B*H, N, d], then the fp32 row
+// vectors D and LSE*log2(e), each [B*H, Npad]; every section 256-byte aligned.
 size_t ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   const size_t rows = size_t(B) * size_t(H) * size_t(N);
-  return round_up(rows * size_t(d) * 4, kWsAlign) + 2 * round_up(rows * 4, kWsAlign);
+  const size_t prow = size_t(B) * size_t(H) * size_t(padded_rows(N));
+  return round_up(rows * size_t(d) * 4, kWsAlign) + 2 * round_up(prow * 4, kWsAlign);
 }
 
 // Pointers of the backward pass; `used` selects the ones a stage reads or
@@ -120,6 +127,7 @@ int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t
   if (any_alias(outs, n_out, ins, n_in)) return FA_ERR_ALIASING;
 
   const size_t rows = size_t(B * H * N);
+  const size_t prow = size_t(B * H) * size_t(padded_rows(N));
   char* ws = static_cast<char*>(p.ws);
   a->q = static_cast<const uint16_t*>(p.q);
   a->k = static_cast<const uint16_t*>(p.k);
@@ -133,8 +141,9 @@ int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t
   a->dq_acc = reinterpret_cast<float*>(ws);
   a->delta = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign));
   a->lse2 = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign) +
-                                     round_up(rows * 4, kWsAlign));
+                                     round_up(prow * 4, kWsAlign));
   a->N = int(N);
+  a->Npad = int(padded_rows(N));
   a->BH = int(B * H);
   a->scale = scale;
   a->scale_log2 = scale * 1.4426950408889634f;

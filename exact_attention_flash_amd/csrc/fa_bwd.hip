@@ -35,16 +35,24 @@
 namespace fa {
 
 // ------------------------------------------------------------------ pre pass
+// Row pass over [B*H, Npad] rows (Npad = N rounded up to the query block):
+// D = rowsum(dO o O) and LSE * log2(e) for real rows, D = 0 and +inf for the
+// padding rows (so a padded query gets P = 0 in the main pass), and the dQ
+// accumulator rows cleared.
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;       // threads per row (16-byte chunks)
   constexpr int RPB = 256 / TPR;   // rows per workgroup
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int64_t rr = (int64_t)blockIdx.x * RPB + tid / TPR;
   const int ch = tid % TPR;
-  const int64_t rows = (int64_t)a.BH * a.N;
+  const int64_t rows = (int64_t)a.BH * a.Npad;
+  const int64_t bh = rr / a.Npad;
+  const int q = (int)(rr - bh * a.Npad);
+  const bool real = rr < rows && q < a.N;
+  const int64_t row = bh * a.N + q;  // row of the [B*H, N] tensors
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const u32x4 o = load_global<u32x4>(a.o + row * D + ch * 8);
     const u32x4 d = load_global<u32x4>(a.dout + row * D + ch * 8);
 #pragma unroll
@@ -58,9 +66,9 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && ch == 0) {
-    a.delta[row] = acc;
-    a.lse2[row] = a.lse[row] * kLog2e;
+  if (rr < rows && ch == 0) {
+    a.delta[rr] = acc;
+    a.lse2[rr] = real ? a.lse[row] * kLog2e : INFINITY;
   }
 }
 
@@ -71,173 +79,259 @@ struct BwdCfg {
   static constexpr int NT = NW * 64;
   static constexpr int KW = 32;            // keys per wave
   static constexpr int BCK = NW * KW;      // keys per workgroup
-  static constexpr int BRQ = 64;           // queries per iteration
-  static constexpr int QP = D + 8;         // Q / dO row-major pitch
-  static constexpr int TP = BRQ + 8;       // Q^T / dO^T pitch
-  static constexpr int SP = BCK + 8;       // dS pitch ([query][key])
-  static constexpr int KTP = BCK + 8;      // K^T pitch ([d][key])
+  static constexpr int BRQ = kBwdQueryBlock;  // queries per iteration
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int QT = BRQ * D;       // elements of a Q or dO tile
+  static constexpr int KT = BCK * D;       // elements of the K tile
+  static constexpr int ST = BCK * BRQ;     // elements of a dS^T tile
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) fa_bwd_main_kernel(BwdArgs a) {
+// Asynchronous copy of query block [q0, q0 + BRQ) of Q and dO (natural row
+// order, swizzled chunks) and of its LSE*log2(e) and D rows into one stage.
+// Rows past N copy row N - 1 (their LSE is +inf, so they get P = 0).
+template <int D>
+__device__ __forceinline__ void issue_q_tile(const uint16_t* Qh, const uint16_t* dOh,
+                                             const float* lse2h, const float* delh,
+                                             uint16_t* Qs, uint16_t* dOs, float* vec, int q0,
+                                             int N, int w, int lane) {
   using C = BwdCfg<D>;
-  constexpr int BRQ = C::BRQ, BCK = C::BCK, QP = C::QP, TP = C::TP, SP = C::SP, KTP = C::KTP;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BRQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BRQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[BRQ * SP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * KTP];
-  __shared__ __attribute__((aligned(16))) float lse_s[BRQ];
-  __shared__ __attribute__((aligned(16))) float del_s[BRQ];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, g = lane >> 5;
-  const int N = a.N;
-  const int nkb = (N + BCK - 1) / BCK;
-
-  // Workgroup -> (head, key block), XCD-contiguous like the forward pass.
-  // Causal key blocks near the start see the most query blocks, so the
-  // natural order is already heaviest first.
-  const int total = gridDim.x;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int bh = L / nkb;
-  const int kb = L - bh * nkb;
-  const int kb0 = kb * BCK;
-  const int kw0 = kb0 + w * C::KW;
-  const int key = kw0 + c32;  // the key this lane owns
-
-  const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* Qh = a.q + hoff;
-  const uint16_t* dOh = a.dout + hoff;
-  const float* lse2h = a.lse2 + (int64_t)bh * N;
-  const float* delh = a.delta + (int64_t)bh * N;
-  float* dQh = a.dq_acc + hoff;
-
-  // K and V of this lane's key as B operands (K[key][16 kc + 8 g + 0..7]).
-  bf16x8 kf[D / 16], vf[D / 16];
+  constexpr int COPIES = C::BRQ * C::CPR / C::NT;
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    const int64_t off = hoff + (int64_t)key * D + kc * 16 + g * 8;
-    kf[kc] = key < N ? load_global<bf16x8>(a.k + off) : zero_bf16x8();
-    vf[kc] = key < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
+  for (int t = 0; t < COPIES; ++t) {
+    const int slot = (t * C::NW + w) * 64 + lane;
+    const int row = slot / C::CPR;
+    const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
+    const int qq = min(q0 + row, N - 1);
+    const int base = (t * C::NW + w) * 64 * 8;
+    load_lds16(Qh + (int64_t)qq * D + lc * 8, Qs + base);
+    load_lds16(dOh + (int64_t)qq * D + lc * 8, dOs + base);
   }
-  {
-    TransTile<BCK, D, C::NT> kt;
-    kt.load(a.k + hoff, kb0, N, tid);
-    kt.store(Kt, KTP, tid);
+  // LSE*log2(e) then D: 2 x BRQ floats = BRQ / 2 lanes of 16 bytes (padded rows)
+  if (w == 0 && lane < C::BRQ / 2) {
+    const int half = C::BRQ / 4;  // lanes per vector
+    const float* src = lane < half ? lse2h + q0 + 4 * lane : delh + q0 + 4 * (lane - half);
+    load_lds16(src, vec);
   }
+}
 
+// Shared memory of the key-block pass: the K block (for the K^T operand of
+// dS K), double-buffered Q / dO tiles with their LSE*log2(e) and D rows, and
+// double-buffered dS^T tiles ([key][query], bf16).
+template <int D>
+struct BwdSmem {
+  using C = BwdCfg<D>;
+  uint16_t k[C::KT];
+  uint16_t q[2][C::QT];
+  uint16_t dout[2][C::QT];
+  uint16_t dst[2][C::ST];
+  float vec[2][2 * C::BRQ];
+};
+
+// One workgroup of the key-block pass: per-lane state and the steps of one
+// query block.  Stage indices are template parameters so every LDS offset
+// that does not depend on the lane is a compile-time immediate.
+template <int D, bool CAUSAL>
+struct BwdBlock {
+  using C = BwdCfg<D>;
+  static constexpr int BRQ = C::BRQ, BCK = C::BCK;
+
+  BwdSmem<D>& sm;
+  const BwdArgs& a;
+  int w, lane, c32, g, N, bh, kb0, kw0, key, nqb;
+  int64_t hoff;
+  const uint16_t* Qh;
+  const uint16_t* dOh;
+  const float* lse2h;
+  const float* delh;
+  float* dQh;
+  float sl2;
+  TrLane<D> trd;       // transposed reads of the Q, dO and K tiles
+  TrLane<BRQ> trs;     // transposed reads of the dS^T tile
+  RowLane<D> rowd;     // row reads of the Q and dO tiles
+  int dsw_base, dsw_u; // dS^T row writes
+  int kr_base, kr_u;   // row reads of this lane's key in the K block
+  bf16x8 vf[D / 16];
   f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: lane holds [32 db + 8(i/4) + 4g + i%4][key]
+
+  __device__ __forceinline__ BwdBlock(BwdSmem<D>& sm_, const BwdArgs& a_, int bh_, int kb0_)
+      : sm(sm_), a(a_), trd(threadIdx.x & 63), trs(threadIdx.x & 63), rowd(threadIdx.x & 63) {
+    const int tid = threadIdx.x;
+    w = tid >> 6;
+    lane = tid & 63;
+    c32 = lane & 31;
+    g = lane >> 5;
+    N = a.N;
+    bh = bh_;
+    kb0 = kb0_;
+    kw0 = kb0 + w * C::KW;
+    key = kw0 + c32;
+    nqb = (N + BRQ - 1) / BRQ;
+    hoff = (int64_t)bh * N * D;
+    Qh = a.q + hoff;
+    dOh = a.dout + hoff;
+    lse2h = a.lse2 + (int64_t)bh * a.Npad;
+    delh = a.delta + (int64_t)bh * a.Npad;
+    dQh = a.dq_acc + hoff;
+    sl2 = a.scale_log2;
+    dsw_base = (w * C::KW + c32) * BRQ;
+    dsw_u = g ^ chunk_swizzle<BRQ>(c32);
+    kr_base = (w * C::KW + c32) * D;
+    kr_u = g ^ chunk_swizzle<D>(c32);
+  }
+
+  __device__ __forceinline__ void issue_k_block() {
+    constexpr int COPIES = BCK * C::CPR / C::NT;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
-
-  const float sl2 = a.scale_log2;
-  const int nqb = (N + BRQ - 1) / BRQ;
-  const int i0 = CAUSAL ? kb0 / BRQ : 0;
-
-  RowTile<BRQ, D, C::NT, true> qrow, dorow;
-  TransTile<BRQ, D, C::NT> qtr, dotr;
-
-  for (int i = i0; i < nqb; ++i) {
-    const int q0 = i * BRQ;
-    qrow.load(Qh, q0, N, tid);
-    dorow.load(dOh, q0, N, tid);
-    qtr.load(Qh, q0, N, tid);
-    dotr.load(dOh, q0, N, tid);
-    __syncthreads();  // previous iteration is done with every LDS tile
-    qrow.store(Qs, QP, tid);
-    dorow.store(dOs, QP, tid);
-    qtr.store(Qt, TP, tid);
-    dotr.store(dOt, TP, tid);
-    if (tid < BRQ) {
-      const int q = q0 + tid;
-      lse_s[tid] = q < N ? lse2h[q] : INFINITY;  // padded rows get P = 0
-      del_s[tid] = q < N ? delh[q] : 0.f;
+    for (int t = 0; t < COPIES; ++t) {
+      const int slot = (t * C::NW + w) * 64 + lane;
+      const int row = slot / C::CPR;
+      const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
+      const int kk = min(kb0 + row, N - 1);
+      load_lds16(a.k + hoff + (int64_t)kk * D + lc * 8, sm.k + (t * C::NW + w) * 64 * 8);
     }
-    __syncthreads();
+  }
 
+  __device__ __forceinline__ void load_kv_operands() {
 #pragma unroll
-    for (int qs = 0; qs < BRQ / 32; ++qs) {
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (qs * 32 + c32) * QP + kc * 16 + g * 8);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(dOs + (qs * 32 + c32) * QP + kc * 16 + g * 8);
-        s = mfma32(qa, kf[kc], s);
-        dp = mfma32(da, vf[kc], dp);
-      }
-      // value i <-> query q0 + 32 qs + 16 (i/8) + 8 g + i%8, key `key`
-      const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qs);
-      float p[16], ds[16];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int ql = 32 * qs + 16 * c + 8 * g;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_s + ql);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_s + ql + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(del_s + ql);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(del_s + ql + 4);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int idx = 8 * c + jj;
-          const float lv = jj < 4 ? l0[jj] : l1[jj - 4];
-          const float dv_ = jj < 4 ? d0[jj] : d1[jj - 4];
-          float pv = exp2_fast(fmaf(s[idx], sl2, -lv));
-          if (need_mask) {
-            const int q = q0 + ql + jj;
-            if (key >= N || (CAUSAL && key > q)) pv = 0.f;
-          }
-          p[idx] = pv;
-          ds[idx] = pv * (dp[idx] - dv_);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over this sub-block's 32 queries.
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pb = pack8(p + 8 * c);
-        const bf16x8 sb = pack8(ds + 8 * c);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(dOt + (db * 32 + c32) * TP + qs * 32 + 16 * c + 8 * g);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + (db * 32 + c32) * TP + qs * 32 + 16 * c + 8 * g);
-          dv[db] = mfma32(oa, pb, dv[db]);
-          dk[db] = mfma32(qa, sb, dk[db]);
-        }
-      }
-      // dS (bf16) into LDS as [query][key] for the dQ product.
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int ql = 32 * qs + 16 * (idx >> 3) + 8 * g + (idx & 7);
-        const __bf16 h = (__bf16)ds[idx];
-        dSs[ql * SP + w * C::KW + c32] = __builtin_bit_cast(uint16_t, h);
-      }
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const int64_t off = hoff + (int64_t)key * D + kc * 16 + g * 8;
+      vf[kc] = key < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
     }
-    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
+  }
 
-    // dQ rows q0 .. q0+63 += dS K over the block's 128 keys (scale applied
-    // when converting).  Tasks: (query sub-block, 32-column slice of d).
+  template <int ST>
+  __device__ __forceinline__ void issue_q(int i) {
+    issue_q_tile<D>(Qh, dOh, lse2h, delh, sm.q[ST], sm.dout[ST], sm.vec[ST], i * BRQ, N, w, lane);
+  }
+
+  // dQ rows of query block ib += dS K over the block's keys, from dS^T stage
+  // ST.  Wave w computes 32-column slices: db = w (d = 128) or
+  // (qs, db) = (w / 2, w % 2) (d = 64).
+  template <int ST>
+  __device__ __forceinline__ void dq_block(int ib) {
+    const uint16_t* sd = sm.dst[ST];
+    const TrLane<D> trd = this->trd.fresh();
+    const TrLane<BRQ> trs = this->trs.fresh();
     constexpr int TASKS = (BRQ / 32) * (D / 32);
 #pragma unroll
-    for (int t = w; t < TASKS; t += C::NW) {
+    for (int t0 = 0; t0 < TASKS; t0 += C::NW) {
+      const int t = t0 + w;
       const int qs = t / (D / 32), db = t % (D / 32);
       f32x16 acc = zero16();
 #pragma unroll
       for (int kc = 0; kc < BCK / 16; ++kc) {
-        const bf16x8 sa = *reinterpret_cast<const bf16x8*>(dSs + (qs * 32 + c32) * SP + kc * 16 + g * 8);
-        const bf16x8 kb_ = *reinterpret_cast<const bf16x8*>(Kt + (db * 32 + c32) * KTP + kc * 16 + g * 8);
-        acc = mfma32(sa, kb_, acc);
+        const bf16x8 sa = join_tr(lds_read_tr(sd + trs.off(16 * kc, 32 * qs, 0)),
+                                  lds_read_tr(sd + trs.off(16 * kc, 32 * qs, 1)));
+        const bf16x8 kt = join_tr(lds_read_tr(sm.k + trd.off(16 * kc, 32 * db, 0)),
+                                  lds_read_tr(sm.k + trd.off(16 * kc, 32 * db, 1)));
+        acc = mfma32(sa, kt, acc);
       }
+      // rows qb0 + 8 (idx/4) + 4 g + idx%4, column 32 db + c32
+      const int qb0 = ib * BRQ + 32 * qs;
+      float* base = dQh + (int64_t)(qb0 + 4 * g) * D + db * 32 + c32;
+      if (qb0 + 32 <= N) {
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int q = q0 + qs * 32 + 8 * (idx >> 2) + 4 * g + (idx & 3);
-        if (q < N) atomicAdd(dQh + (int64_t)q * D + db * 32 + c32, acc[idx]);
+        for (int idx = 0; idx < 16; ++idx)
+          atomicAdd(base + (8 * (idx >> 2) + (idx & 3)) * D, acc[idx]);
+      } else {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          if (qb0 + 4 * g + 8 * (idx >> 2) + (idx & 3) < N)
+            atomicAdd(base + (8 * (idx >> 2) + (idx & 3)) * D, acc[idx]);
       }
     }
   }
 
-  // dK = scale * (dS^T Q), dV = P^T dO, rows of this lane's key.
-  if (key < N) {
+  // S, P, dP, dS for query block i (stage ST): dV^T, dK^T accumulate; dS^T
+  // goes to LDS stage ST for the dQ product.
+  template <int ST>
+  __device__ __forceinline__ void kv_block(int i) {
+    const uint16_t* Qt = sm.q[ST];
+    const uint16_t* dOt = sm.dout[ST];
+    const float* lv = sm.vec[ST];
+    uint16_t* sd = sm.dst[ST];
+    const int q0 = i * BRQ;
+    const TrLane<D> trd = this->trd.fresh();
+    const RowLane<D> rowd = this->rowd.fresh();
+    const int kr_base = opaque(this->kr_base), kr_u = opaque(this->kr_u);
+    const int dsw_base = opaque(this->dsw_base), dsw_u = opaque(this->dsw_u);
+#pragma unroll
+    for (int qs = 0; qs < BRQ / 32; ++qs) {
+      // value idx <-> query q0 + 32 qs + 16 (idx/8) + 8 g + idx%8, key `key`
+      const bool skip = CAUSAL && (kw0 > q0 + 32 * qs + 31);
+      float p[16], ds[16];
+      if (!skip) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const int o = rowd.off(32 * qs, kc);
+          const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sm.k + kr_base + (((2 * kc) ^ kr_u) << 3));
+          s = mfma32(*reinterpret_cast<const bf16x8*>(Qt + o), kb, s);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(dOt + o), vf[kc], dp);
+        }
+        const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qs);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int ql = 32 * qs + 16 * c + 8 * g;
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(lv + ql);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(lv + ql + 4);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql + 4);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int idx = 8 * c + jj;
+            const float lse = jj < 4 ? l0[jj] : l1[jj - 4];
+            const float dlt = jj < 4 ? d0[jj] : d1[jj - 4];
+            float pv = exp2_fast(fmaf(s[idx], sl2, -lse));
+            if (need_mask) {
+              const int q = q0 + ql + jj;
+              if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+            }
+            p[idx] = pv;
+            ds[idx] = pv * (dp[idx] - dlt);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the sub-block's 32 queries.
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pb = pack8(p + 8 * c);
+          const bf16x8 sb = pack8(ds + 8 * c);
+          const int R0 = 32 * qs + 16 * c;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const int o0 = trd.off(R0, 32 * db, 0), o1 = trd.off(R0, 32 * db, 1);
+            const bf16x8 oa = join_tr(lds_read_tr(dOt + o0), lds_read_tr(dOt + o1));
+            const bf16x8 qa = join_tr(lds_read_tr(Qt + o0), lds_read_tr(Qt + o1));
+            dv[db] = mfma32(oa, pb, dv[db]);
+            dk[db] = mfma32(qa, sb, dk[db]);
+          }
+          // dS^T row `key`, 8 consecutive queries (16 bytes)
+          *reinterpret_cast<bf16x8*>(sd + dsw_base + (((4 * qs + 2 * c) ^ dsw_u) << 3)) = sb;
+        }
+      } else {
+        const bf16x8 z = zero_bf16x8();
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          *reinterpret_cast<bf16x8*>(sd + dsw_base + (((4 * qs + 2 * c) ^ dsw_u) << 3)) = z;
+      }
+    }
+  }
+
+  // One iteration of the steady state: prefetch block i + 1, dQ of block
+  // i - 1, then block i.
+  template <int ST>
+  __device__ __forceinline__ void step(int i) {
+    if (i + 1 < nqb) issue_q<ST ^ 1>(i + 1);
+    dq_block<ST ^ 1>(i - 1);
+    kv_block<ST>(i);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void store_dkdv() {
+    if (key >= N) return;
     uint16_t* dKrow = a.dk + hoff + (int64_t)key * D;
     uint16_t* dVrow = a.dv + hoff + (int64_t)key * D;
     const float sc = a.scale;
@@ -255,6 +349,51 @@ __global__ void __launch_bounds__(256) fa_bwd_main_kernel(BwdArgs a) {
         *reinterpret_cast<u32x2*>(dVrow + col) = vv;
       }
   }
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) fa_bwd_main_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  static_assert(C::BRQ == 64, "two 32-query sub-blocks per iteration");
+  __shared__ __attribute__((aligned(1024))) BwdSmem<D> sm;
+
+  const int N = a.N;
+  const int nkb = (N + C::BCK - 1) / C::BCK;
+  // Workgroup -> (head, key block), XCD-contiguous like the forward pass.
+  // Causal key blocks near the start see the most query blocks, so the
+  // natural order is already heaviest first.
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int bh = L / nkb;
+  const int kb = L - bh * nkb;
+
+  BwdBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
+  const int nqb = blk.nqb;
+  const int i0 = CAUSAL ? blk.kb0 / C::BRQ : 0;
+  blk.issue_k_block();
+  blk.template issue_q<0>(i0);
+  blk.load_kv_operands();
+  wait_vmem();
+  __syncthreads();
+
+  // block i0 (stage 0) has no previous dQ to do
+  if (i0 + 1 < nqb) blk.template issue_q<1>(i0 + 1);
+  blk.template kv_block<0>(i0);
+  wait_vmem();
+  __syncthreads();
+  int i = i0 + 1;
+  for (; i + 1 < nqb; i += 2) {
+    blk.template step<1>(i);
+    blk.template step<0>(i + 1);
+  }
+  if (i < nqb) {
+    blk.template step<1>(i);
+    blk.template dq_block<1>(nqb - 1);
+  } else {
+    blk.template dq_block<0>(nqb - 1);
+  }
+  blk.store_dkdv();
 }
 
 // ------------------------------------------------------------------ dQ convert
@@ -274,7 +413,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a, int64_t n8) {
 
 template <int D>
 static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.BH * a.N;
+  const int64_t rows = (int64_t)a.BH * a.Npad;
   const int64_t rpb = 256 / (D / 8);
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
                      stream, a);

@@ -207,16 +207,20 @@ __device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
-// XOR swizzle of the 16-byte chunks of an unpadded row-major LDS tile, so
-// that the MFMA operand reads (16 rows at one chunk; 4 rows at 4 chunks for
-// the transposed reads) hit distinct banks.
+// XOR swizzle of the 16-byte chunks of an unpadded row-major LDS tile whose
+// rows hold D bf16 values (D = 128: 16 chunks; D = 64: 8 chunks), so that the
+// MFMA operand reads (16 consecutive rows at one chunk; 4 rows at 2-4 chunks
+// for the transposed reads) hit distinct banks.  It is linear over the low 4
+// bits of the row (period 16), so rows that differ by a multiple of 16 share
+// it, and rows r and r + 4 (r % 8 < 4) differ by chunk bit 0.
 template <int D>
 __device__ __forceinline__ int chunk_swizzle(int row) {
   if constexpr (D == 128) {
     return ((row & 1) ? 0x6 : 0) ^ ((row & 2) ? 0xC : 0) ^ ((row & 4) ? 0x1 : 0) ^
            ((row & 8) ? 0x8 : 0);
   } else {
-    return ((row << 1) ^ (row >> 2)) & 7;
+    return ((row & 1) ? 0x2 : 0) ^ ((row & 2) ? 0x4 : 0) ^ ((row & 4) ? 0x1 : 0) ^
+           ((row & 8) ? 0x2 : 0);
   }
 }
 
@@ -225,5 +229,72 @@ template <int D>
 __device__ __forceinline__ int swz_off(int row, int col) {
   return row * D + ((((col >> 3) ^ chunk_swizzle<D>(row))) << 3) + (col & 7);
 }
+
+}  // namespace fa
+
+namespace fa {
+
+// Make the compiler forget what it knows about a per-lane value.  Used on
+// address constants at the top of each loop iteration: without it every LDS
+// address (all loop invariant once the double-buffer stage is a template
+// parameter) is hoisted out of the loop into its own register.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Per-lane constants for transposed reads (lds_read_tr) of a swizzled
+// row-major [rows][D] tile, as MFMA operands with rows = contraction index:
+// the read for row block R0 (a multiple of 16), column block C0 (a multiple
+// of 32) and half `hi` gives lane (c, g) the column C0 + c of rows
+// R0 + 8g + 4hi + 0..3.  Only the XOR with (C0 / 8) ^ hi depends on the
+// compile-time indices, so each read costs two integer operations.
+template <int D>
+struct TrLane {
+  int base;  // lane's row and 8-byte half, in elements
+  int t;     // lane's chunk bits XOR its rows' swizzle
+  TrLane() = default;
+  __device__ __forceinline__ explicit TrLane(int lane) {
+    const int g = lane >> 5, e = (lane >> 2) & 3, q = lane & 3, half = (lane >> 4) & 1;
+    const int r = 8 * g + e;
+    base = r * D + 4 * (q & 1);
+    t = (2 * half + (q >> 1)) ^ chunk_swizzle<D>(r);
+  }
+  __device__ __forceinline__ int off(int R0, int C0, int hi) const {
+    return (R0 + 4 * hi) * D + base + ((((C0 >> 3) ^ hi) ^ t) << 3);
+  }
+  __device__ __forceinline__ TrLane fresh() const {
+    TrLane r = *this;
+    r.base = opaque(base);
+    r.t = opaque(t);
+    return r;
+  }
+};
+
+// Per-lane constants for the row reads of a swizzled [rows][D] tile as the
+// A operand of a 32x32x16 MFMA whose lane c reads row swap23(c) (so its C
+// rows come out in runs of eight): the read for row block R0 (a multiple of
+// 32) and contraction slice kc gives the lane 8 values of row
+// R0 + swap23(c), columns 16 kc + 8 g + 0..7.
+template <int D>
+struct RowLane {
+  int base;
+  int u;
+  RowLane() = default;
+  __device__ __forceinline__ explicit RowLane(int lane) {
+    const int r = swap23(lane & 31);
+    base = r * D;
+    u = (lane >> 5) ^ chunk_swizzle<D>(r);
+  }
+  __device__ __forceinline__ int off(int R0, int kc) const {
+    return R0 * D + base + (((2 * kc) ^ u) << 3);
+  }
+  __device__ __forceinline__ RowLane fresh() const {
+    RowLane r = *this;
+    r.base = opaque(base);
+    r.u = opaque(u);
+    return r;
+  }
+};
 
 }  // namespace fa

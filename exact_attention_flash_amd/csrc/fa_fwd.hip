@@ -78,71 +78,56 @@ __device__ __forceinline__ void issue_kv_tile(const uint16_t* Kh, const uint16_t
   }
 }
 
+// LDS of one forward workgroup: K and V tiles of two stages, each its own
+// object.  Separate objects let the compiler see that the copies into one
+// stage never overlap reads of the other, so it does not wait for the
+// in-flight copies before reading the current tile.
+template <int D>
+struct FwdSmem {
+  uint16_t* k0;
+  uint16_t* v0;
+  uint16_t* k1;
+  uint16_t* v1;
+};
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_kernel(FwdArgs a) {
+struct FwdBlock {
   using C = FwdCfg<D>;
-  constexpr int BC = C::BC, TILE = C::TILE;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K, V]
+  static constexpr int BC = C::BC;
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, g = lane >> 5;
-  const int N = a.N;
-  const int nqb = (N + C::BR - 1) / C::BR;
-
-  // Workgroup -> (head, query block).  Consecutive workgroup ids land on
-  // different XCDs (round robin over 8); give each XCD a contiguous run of
-  // work so the query blocks of one head share that XCD's L2.  Within a head
-  // the heaviest (last) causal blocks go first.
-  const int total = gridDim.x;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int bh = L / nqb;
-  int qb = L - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;
-
-  const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* Qh = a.q + hoff;
-  const uint16_t* Kh = a.k + hoff;
-  const uint16_t* Vh = a.v + hoff;
-  const int q0 = qb * C::BR;
-  const int qw0 = q0 + w * C::QW;
-  const int qrow = qw0 + c32;  // the query this lane owns
-
-  int nt = (N + BC - 1) / BC;
-  if (CAUSAL) nt = min(nt, (q0 + C::BR + BC - 1) / BC);
-
-  issue_kv_tile<D>(Kh, Vh, smem, smem + TILE, 0, N, w, lane);
-
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
+  FwdSmem<D> sm;
+  const uint16_t* Kh;
+  const uint16_t* Vh;
+  int w, lane, c32, g, N, qw0, qrow, nt;
+  float sl2;
+  float m_run;   // running max of scale*log2(e)*s (possibly stale)
+  float l_part;  // this lane's share of the running row sum
   bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc)
-    qf[kc] = qrow < N ? load_global<bf16x8>(Qh + (int64_t)qrow * D + kc * 16 + g * 8)
-                      : zero_bf16x8();
+  f32x16 oacc[D / 32];  // O^T: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
+  TrLane<D> trv;        // transposed reads of the V tile
+  int kbase, ku;        // row reads of the K tile (row c32 of each 32-key block)
 
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s (possibly stale)
-  float l_part = 0.f;       // this lane's share of the running row sum
-  f32x16 oacc[D / 32];      // O^T block: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  const float sl2 = a.scale_log2;
+  template <int ST>
+  __device__ __forceinline__ uint16_t* ktile() const { return ST ? sm.k1 : sm.k0; }
+  template <int ST>
+  __device__ __forceinline__ uint16_t* vtile() const { return ST ? sm.v1 : sm.v0; }
 
-  // transposed-read lane roles (see lds_read_tr)
-  const int tr_g = lane >> 5, tr_e = (lane >> 2) & 3, tr_q = lane & 3, tr_half = (lane >> 4) & 1;
+  template <int ST>
+  __device__ __forceinline__ void issue(int j) {
+    issue_kv_tile<D>(Kh, Vh, ktile<ST>(), vtile<ST>(), j * BC, N, w, lane);
+  }
 
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const uint16_t* Ks = smem + (j & 1) * 2 * TILE;
-    const uint16_t* Vs = Ks + TILE;
-    if (j + 1 < nt) {
-      uint16_t* nk = smem + ((j + 1) & 1) * 2 * TILE;
-      issue_kv_tile<D>(Kh, Vh, nk, nk + TILE, (j + 1) * BC, N, w, lane);
-    }
+  // One key tile from stage ST; prefetches tile j + 1 into the other stage.
+  template <int ST>
+  __device__ __forceinline__ void step(int j) {
+    if (j + 1 < nt) issue<ST ^ 1>(j + 1);
+    const uint16_t* Ks = ktile<ST>();
+    const uint16_t* Vs = vtile<ST>();
     const int k0 = j * BC;
     const bool skip = CAUSAL && (k0 > qw0 + C::QW - 1);
     if (!skip) {
+      const TrLane<D> tr = trv.fresh();
+      const int kb = opaque(kbase), kx = opaque(ku);
       // S^T for the tile: two 32-key blocks.  Value i of s[sb] is the score
       // of key k0 + 32 sb + 16 (i / 8) + 8 g + i % 8 against qrow.
       f32x16 s[BC / 32];
@@ -152,8 +137,8 @@ fa_fwd_kernel(FwdArgs a) {
       for (int kc = 0; kc < D / 16; ++kc)
 #pragma unroll
         for (int sb = 0; sb < BC / 32; ++sb) {
-          const int row = sb * 32 + c32;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + swz_off<D>(row, kc * 16 + g * 8));
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(Ks + sb * 32 * D + kb + (((2 * kc) ^ kx) << 3));
           s[sb] = mfma32(ka, qf[kc], s[sb]);
         }
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
@@ -205,12 +190,10 @@ fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) t[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
         const bf16x8 pb = pack8(t);
-        const int vrow = 16 * kc2 + 8 * tr_g + tr_e;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int vcol = 32 * db + 16 * tr_half + 4 * tr_q;
-          const bf16x8 va = join_tr(lds_read_tr(Vs + swz_off<D>(vrow, vcol)),
-                                    lds_read_tr(Vs + swz_off<D>(vrow + 4, vcol)));
+          const bf16x8 va = join_tr(lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 0)),
+                                    lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 1)));
           oacc[db] = mfma32(va, pb, oacc[db]);
         }
       }
@@ -218,22 +201,89 @@ fa_fwd_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();
   }
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr int TILE = C::TILE;
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const int nqb = (N + C::BR - 1) / C::BR;
+
+  // Workgroup -> (head, query block).  Consecutive workgroup ids land on
+  // different XCDs (round robin over 8); give each XCD a contiguous run of
+  // work so the query blocks of one head share that XCD's L2.  Within a head
+  // the heaviest (last) causal blocks go first.
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int bh = L / nqb;
+  int qb = L - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+
+  const int64_t hoff = (int64_t)bh * N * D;
+  FwdBlock<D, CAUSAL> f;
+  f.sm = FwdSmem<D>{k0s, v0s, k1s, v1s};
+  f.Kh = a.k + hoff;
+  f.Vh = a.v + hoff;
+  f.w = tid >> 6;
+  f.lane = tid & 63;
+  f.c32 = f.lane & 31;
+  f.g = f.lane >> 5;
+  f.N = N;
+  const int q0 = qb * C::BR;
+  f.qw0 = q0 + f.w * C::QW;
+  f.qrow = f.qw0 + f.c32;  // the query this lane owns
+  f.nt = (N + C::BC - 1) / C::BC;
+  if (CAUSAL) f.nt = min(f.nt, (q0 + C::BR + C::BC - 1) / C::BC);
+  f.sl2 = a.scale_log2;
+  f.m_run = -INFINITY;
+  f.l_part = 0.f;
+  f.trv = TrLane<D>(f.lane);
+  f.kbase = f.c32 * D;
+  f.ku = f.g ^ chunk_swizzle<D>(f.c32);
+
+  f.template issue<0>(0);
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
+  const uint16_t* Qh = a.q + hoff;
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc)
+    f.qf[kc] = f.qrow < N ? load_global<bf16x8>(Qh + (int64_t)f.qrow * D + kc * 16 + f.g * 8)
+                          : zero_bf16x8();
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) f.oacc[db] = zero16();
+  wait_vmem();
+  __syncthreads();
+
+  int j = 0;
+  for (; j + 1 < f.nt; j += 2) {
+    f.template step<0>(j);
+    f.template step<1>(j + 1);
+  }
+  if (j < f.nt) f.template step<0>(j);
 
   // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
-  const float l = l_part + swap_halves(l_part);
-  if (qrow < N) {
+  const float l = f.l_part + swap_halves(f.l_part);
+  if (f.qrow < N) {
     const float inv = 1.f / l;
-    uint16_t* Orow = a.o + hoff + (int64_t)qrow * D;
+    uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         u32x2 val;
-        val.x = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
-        val.y = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * g) = val;
+        val.x = pack2(f.oacc[db][4 * r4 + 0] * inv, f.oacc[db][4 * r4 + 1] * inv);
+        val.y = pack2(f.oacc[db][4 * r4 + 2] * inv, f.oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * f.g) = val;
       }
-    if (g == 0) a.lse[(int64_t)bh * N + qrow] = (m_run + log2_fast(l)) * kLn2;
+    if (f.g == 0) a.lse[(int64_t)bh * N + f.qrow] = (f.m_run + log2_fast(l)) * kLn2;
   }
 }
 

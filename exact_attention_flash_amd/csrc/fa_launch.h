@@ -19,6 +19,10 @@ struct FwdArgs {
   float scale_log2;   // softmax_scale * log2(e), > 0
 };
 
+// Query rows per block of the backward key-block pass; the row vectors in
+// the backward workspace are padded to a multiple of it.
+constexpr int kBwdQueryBlock = 64;
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -30,9 +34,10 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dq_acc;      // workspace: fp32 [B, H, N, d]
-  float* delta;       // workspace: fp32 [B, H, N], rowsum(dO o O)
-  float* lse2;        // workspace: fp32 [B, H, N], LSE * log2(e)
+  float* delta;       // workspace: fp32 [B*H, Npad], rowsum(dO o O), 0 on padding
+  float* lse2;        // workspace: fp32 [B*H, Npad], LSE * log2(e), +inf on padding
   int N;
+  int Npad;           // N rounded up to kBwdQueryBlock
   int BH;
   float scale;        // softmax_scale, > 0
   float scale_log2;   // softmax_scale * log2(e)

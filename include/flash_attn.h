@@ -87,9 +87,10 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape: an fp32
- * dQ accumulator [B, H, N, d] and two fp32 row vectors [B, H, N] (the
- * rowsum(dO o O) term and LSE in base 2), each section rounded up to 256
- * bytes.  Returns 0 for an empty problem and for invalid sizes.
+ * dQ accumulator [B, H, N, d] and two fp32 row vectors [B*H, Npad] (the
+ * rowsum(dO o O) term and LSE in base 2; Npad is N rounded up to a multiple
+ * of 64), each section rounded up to 256 bytes.  Returns 0 for an empty
+ * problem and for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 

@@ -57,7 +57,10 @@ def test_workspace_bytes():
     rows = 4 * 16 * 4096
     want = (rows * 128 * 4 + 255) // 256 * 256 + 2 * ((rows * 4 + 255) // 256 * 256)
     assert lib.flash_attn_bwd_workspace_bytes(4, 16, 4096, 128) == want
+    # row vectors are padded to whole 64-row query blocks per head
     assert lib.flash_attn_bwd_workspace_bytes(1, 1, 1, 64) == 256 + 2 * 256
+    want = (3 * 100 * 128 * 4 + 255) // 256 * 256 + 2 * ((3 * 128 * 4 + 255) // 256 * 256)
+    assert lib.flash_attn_bwd_workspace_bytes(1, 3, 100, 128) == want
     assert lib.flash_attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert lib.flash_attn_bwd_workspace_bytes(1, 1, 10, 96) == 0
     assert lib.flash_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
