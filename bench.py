@@ -2,7 +2,8 @@
 """Throughput of the fused attention hot path on one MI355X.
 
 One step is the whole path once: the forward kernel (O, LSE), then the three
-backward stages (row pass, key-block pass, dQ conversion), on causal
+backward stages (row pass, key-block pass for dK/dV, query-block pass for
+dQ), on causal
 attention with B=4, H=16, N=4096, d=128 in bf16 (the forward+backward
 workload; Q, K, V, dO i.i.d. N(0, 1) from a fixed seed, already resident in
 HBM before timing starts).
@@ -147,7 +148,7 @@ def main() -> int:
         fa.flash_attn_bwd_kv_blocks(do, q, k, v, dk, dv, ws, causal=causal, softmax_scale=scale)
         if evs:
             evs[3].record(stream)
-        fa.flash_attn_bwd_convert_dq(ws, dq, softmax_scale=scale)
+        fa.flash_attn_bwd_q_blocks(do, q, k, v, dq, ws, causal=causal, softmax_scale=scale)
         if evs:
             evs[4].record(stream)
 
@@ -163,16 +164,20 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_main", "fa_bwd_dq"]
+    names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_kv", "fa_bwd_q"]
     avg_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps
               for j, n in enumerate(names)}
     rows = B * H * N
     f_fwd, f_bwd = wl.flops_fwd(causal), wl.flops_bwd(causal)
-    work = {  # (bound, algorithmic work per launch, unit)
+    # (bound, algorithmic work per launch).  The backward's 2.5 x forward flop
+    # convention is five N^2 d products per head: the key-block pass does four
+    # of them (S, dP, dV, dK) and the query-block pass the fifth (dQ) plus a
+    # recompute of S and dP that the convention does not count.
+    work = {
         "fa_fwd": ("mfma", f_fwd),
-        "fa_bwd_pre": ("hbm", rows * d * 2 * 2 + rows * 4 + rows * d * 4 + rows * 4 * 2),
-        "fa_bwd_main": ("mfma", f_bwd),
-        "fa_bwd_dq": ("hbm", rows * d * 4 + rows * d * 2),
+        "fa_bwd_pre": ("hbm", rows * d * 2 * 2 + rows * 4 + rows * 4 * 2),
+        "fa_bwd_kv": ("mfma", f_bwd * 4 / 5),
+        "fa_bwd_q": ("mfma", f_bwd * 1 / 5),
     }
     kernels = {}
     for n in names:
@@ -197,7 +202,7 @@ def main() -> int:
     }
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = f_fwd / (avg_ms["fa_fwd"] * 1e-3) / 1e12
-    bwd_ms = avg_ms["fa_bwd_pre"] + avg_ms["fa_bwd_main"] + avg_ms["fa_bwd_dq"]
+    bwd_ms = avg_ms["fa_bwd_pre"] + avg_ms["fa_bwd_kv"] + avg_ms["fa_bwd_q"]
     line = {
         "metric": "attention TFLOP/s (fwd+bwd) at 1 GPU",
         "value": round(value, 2),

@@ -12,7 +12,7 @@ __all__ = [
     "flash_attn_bwd_workspace_bytes",
     "flash_attn_bwd_preprocess",
     "flash_attn_bwd_kv_blocks",
-    "flash_attn_bwd_convert_dq",
+    "flash_attn_bwd_q_blocks",
     "flash_attn_status_string",
     "FlashAttnError",
     "load_library",

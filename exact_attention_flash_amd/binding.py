@@ -56,9 +56,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.flash_attn_bwd_kv_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                  i64, i64, i64, i64, ci, fl, vp]
         lib.flash_attn_bwd_kv_blocks.restype = ci
-        lib.flash_attn_bwd_convert_dq.argtypes = [vp, ctypes.c_size_t, vp, i64, i64, i64, i64,
-                                                  fl, vp]
-        lib.flash_attn_bwd_convert_dq.restype = ci
+        lib.flash_attn_bwd_q_blocks.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                i64, i64, i64, i64, ci, fl, vp]
+        lib.flash_attn_bwd_q_blocks.restype = ci
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -183,7 +183,7 @@ def flash_attn_bwd_kv_blocks(dout: torch.Tensor, q: torch.Tensor, k: torch.Tenso
                              v: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
                              workspace: torch.Tensor, causal: bool = False,
                              softmax_scale: float | None = None, stream=None) -> None:
-    """Stage 2 of the backward pass (key-block pass: dK, dV, dQ accumulator)."""
+    """Stage 2 of the backward pass (key-block pass: dK, dV)."""
     B, H, N, d = _check_tensors(q, k, v, dout, dk, dv, names="q,k,v,dout,dk,dv")
     scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
     wp, wb = _ws(workspace, q.device)
@@ -195,13 +195,16 @@ def flash_attn_bwd_kv_blocks(dout: torch.Tensor, q: torch.Tensor, k: torch.Tenso
     _check(st)
 
 
-def flash_attn_bwd_convert_dq(workspace: torch.Tensor, dq: torch.Tensor,
-                              softmax_scale: float | None = None, stream=None) -> None:
-    """Stage 3 of the backward pass (dQ accumulator to bf16)."""
-    B, H, N, d = _check_tensors(dq, names="dq")
+def flash_attn_bwd_q_blocks(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                            v: torch.Tensor, dq: torch.Tensor, workspace: torch.Tensor,
+                            causal: bool = False, softmax_scale: float | None = None,
+                            stream=None) -> None:
+    """Stage 3 of the backward pass (query-block pass: dQ)."""
+    B, H, N, d = _check_tensors(q, k, v, dout, dq, names="q,k,v,dout,dq")
     scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
-    wp, wb = _ws(workspace, dq.device)
-    with torch.cuda.device(dq.device):
-        st = load_library().flash_attn_bwd_convert_dq(wp, wb, dq.data_ptr(), B, H, N, d, scale,
-                                                      _stream_ptr(dq.device, stream))
+    wp, wb = _ws(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = load_library().flash_attn_bwd_q_blocks(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(), wp, wb,
+            B, H, N, d, int(bool(causal)), scale, _stream_ptr(q.device, stream))
     _check(st)

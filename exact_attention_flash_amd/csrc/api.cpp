@@ -69,12 +69,12 @@ int64_t padded_rows(int64_t N) {
   return (N + fa::kBwdQueryBlock - 1) / fa::kBwdQueryBlock * fa::kBwdQueryBlock;
 }
 
-// Workspace layout: fp32 dQ accumulator [B*H, N, d], then the fp32 row
-// vectors D and LSE*log2(e), each [B*H, Npad]; every section 256-byte aligned.
+// Workspace layout: the fp32 row vectors D and LSE*log2(e), each
+// [B*H, Npad], each section 256-byte aligned.
 size_t ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  const size_t rows = size_t(B) * size_t(H) * size_t(N);
+  (void)d;
   const size_t prow = size_t(B) * size_t(H) * size_t(padded_rows(N));
-  return round_up(rows * size_t(d) * 4, kWsAlign) + 2 * round_up(prow * 4, kWsAlign);
+  return 2 * round_up(prow * 4, kWsAlign);
 }
 
 // Pointers of the backward pass; `used` selects the ones a stage reads or
@@ -126,7 +126,6 @@ int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t
   }
   if (any_alias(outs, n_out, ins, n_in)) return FA_ERR_ALIASING;
 
-  const size_t rows = size_t(B * H * N);
   const size_t prow = size_t(B * H) * size_t(padded_rows(N));
   char* ws = static_cast<char*>(p.ws);
   a->q = static_cast<const uint16_t*>(p.q);
@@ -138,10 +137,8 @@ int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t
   a->dq = static_cast<uint16_t*>(p.dq);
   a->dk = static_cast<uint16_t*>(p.dk);
   a->dv = static_cast<uint16_t*>(p.dv);
-  a->dq_acc = reinterpret_cast<float*>(ws);
-  a->delta = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign));
-  a->lse2 = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign) +
-                                     round_up(prow * 4, kWsAlign));
+  a->delta = reinterpret_cast<float*>(ws);
+  a->lse2 = reinterpret_cast<float*>(ws + round_up(prow * 4, kWsAlign));
   a->N = int(N);
   a->Npad = int(padded_rows(N));
   a->BH = int(B * H);
@@ -198,8 +195,8 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (st != FA_OK || a.BH == 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (fa::launch_bwd_pre(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_main(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_dq(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_kv(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_q(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -223,20 +220,21 @@ int flash_attn_bwd_kv_blocks(const void* q, const void* k, const void* v, const 
   const int st = prepare_bwd(p, kQ | kK | kV | kDout | kDk | kDv | kWs, workspace_bytes, B, H, N,
                              d, softmax_scale, &a);
   if (st != FA_OK || a.BH == 0) return st;
-  return fa::launch_bwd_main(a, int(d), causal != 0, static_cast<hipStream_t>(stream)) ==
+  return fa::launch_bwd_kv(a, int(d), causal != 0, static_cast<hipStream_t>(stream)) ==
                  hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int flash_attn_bwd_convert_dq(void* workspace, size_t workspace_bytes, void* dq, int64_t B,
-                              int64_t H, int64_t N, int64_t d, float softmax_scale,
-                              void* stream) {
-  const BwdPtrs p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr, nullptr,
-                  workspace};
+int flash_attn_bwd_q_blocks(const void* q, const void* k, const void* v, const void* dout,
+                            void* dq, void* workspace, size_t workspace_bytes, int64_t B,
+                            int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
+                            void* stream) {
+  const BwdPtrs p{q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, workspace};
   fa::BwdArgs a;
-  const int st = prepare_bwd(p, kDq | kWs, workspace_bytes, B, H, N, d, softmax_scale, &a);
+  const int st = prepare_bwd(p, kQ | kK | kV | kDout | kDq | kWs, workspace_bytes, B, H, N, d,
+                             softmax_scale, &a);
   if (st != FA_OK || a.BH == 0) return st;
-  return fa::launch_bwd_dq(a, int(d), static_cast<hipStream_t>(stream)) == hipSuccess
-             ? FA_OK : FA_ERR_HIP;
+  return fa::launch_bwd_q(a, int(d), causal != 0, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* flash_attn_status_string(int status) {

@@ -1,34 +1,25 @@
 // Fused attention backward for gfx950 (recompute from the stored LSE).
 //
 // Method ("FlashAttention 的基本原理", section 2.4; "FlashAttention 系列技术
-// 详解", section "反向传播步骤"; CMU 15-442/642 notes, section
-// "为什么前向和反向的并行化策略不同"): the scores are recomputed block by
-// block, and because LSE is known the probabilities P = exp(scale*S - LSE)
-// are final at once, with no running max.  Then
-//   dV += P^T dO,   dP = dO V^T,   dS = P o (dP - D),   D_i = sum_c dO_ic O_ic,
-//   dK += scale * dS^T Q,   dQ += scale * dS K.
-// The work is split over key blocks (each workgroup owns one K/V block and
-// accumulates its dK, dV in registers); every key block adds into the same
-// dQ rows, so dQ is accumulated in an fp32 buffer with atomic adds and
-// converted to bf16 at the end, as the CMU notes describe.
+// 详解", section "反向传播步骤"): the scores are recomputed block by block, and
+// because LSE is known the probabilities P = exp(scale*S - LSE) are final at
+// once, with no running max.  Then
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   D_i = sum_c dO_ic O_ic,
+//   dK = scale * dS^T Q,   dQ = scale * dS K.
+// The CMU 15-442/642 notes (section "为什么前向和反向的并行化策略不同")
+// parallelise the backward pass over key blocks and accumulate dQ across
+// key blocks with atomic adds in device memory.  On MI355X that accumulation
+// is the bottleneck: fp32 atomics retire at about one 4-byte add per clock
+// per L2 channel, and the dQ adds alone would take longer than the whole
+// rest of the pass.  So dQ gets its own pass, parallel over query blocks
+// like the forward pass, which recomputes S and dP for its rows (two more
+// GEMMs per block pair) and needs no atomics: dQ is deterministic.
 //
 // Three kernels on the caller's stream:
-//   fa_bwd_pre   D = rowsum(dO o O), LSE * log2(e), dQ accumulator := 0
-//   fa_bwd_main  one workgroup per (batch, head, 128-key block)
-//   fa_bwd_dq    dQ = bf16(scale * dQ accumulator)
-//
-// gfx950 mapping of fa_bwd_main (4 waves, wave w owns keys 32w .. 32w+31 of
-// the block; query blocks of 64 rows are streamed through LDS):
-//  * S = Q K^T and dP = dO V^T come out of v_mfma_f32_32x32x16_bf16 with a
-//    lane owning one key and 16 queries; Q and dO rows sit in LDS in swap23
-//    order so those 16 queries are two runs of eight consecutive rows;
-//  * in that layout P and dS, rounded to bf16, are directly the B operands
-//    of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T staged transposed);
-//  * dQ needs dS with keys as the contraction index, so dS goes through LDS
-//    once; each wave then computes a 32-column slice of dS K against K^T
-//    (kept in LDS for the workgroup's lifetime) and adds it into the fp32
-//    accumulator: a lane owns one column, so each atomic instruction covers
-//    whole 128-byte row segments.
+//   fa_bwd_pre   D = rowsum(dO o O) and LSE * log2(e), padded to whole
+//                64-row query blocks (D = 0, LSE = +inf on padding rows)
+//   fa_bwd_kv    one workgroup per (batch, head, 128-key block): dK, dV
+//   fa_bwd_q     one workgroup per (batch, head, 128-query block): dQ
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -37,8 +28,7 @@ namespace fa {
 // ------------------------------------------------------------------ pre pass
 // Row pass over [B*H, Npad] rows (Npad = N rounded up to the query block):
 // D = rowsum(dO o O) and LSE * log2(e) for real rows, D = 0 and +inf for the
-// padding rows (so a padded query gets P = 0 in the main pass), and the dQ
-// accumulator rows cleared.
+// padding rows (so a padded query gets P = 0 in the key-block pass).
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;       // threads per row (16-byte chunks)
@@ -60,9 +50,6 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
       acc = fmaf(bf16_to_f32((uint16_t)(o[j] & 0xffffu)), bf16_to_f32((uint16_t)(d[j] & 0xffffu)), acc);
       acc = fmaf(bf16_to_f32((uint16_t)(o[j] >> 16)), bf16_to_f32((uint16_t)(d[j] >> 16)), acc);
     }
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(a.dq_acc + row * D + ch * 8) = z;
-    *reinterpret_cast<f32x4*>(a.dq_acc + row * D + ch * 8 + 4) = z;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -72,35 +59,33 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ main pass
+// ------------------------------------------------------------------ key-block pass
 template <int D>
-struct BwdCfg {
-  static constexpr int NW = 4;
+struct KvCfg {
+  static constexpr int NW = 8;             // waves per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int KW = 32;            // keys per wave
+  static constexpr int KW = 16;            // keys per wave
   static constexpr int BCK = NW * KW;      // keys per workgroup
   static constexpr int BRQ = kBwdQueryBlock;  // queries per iteration
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int QT = BRQ * D;       // elements of a Q or dO tile
-  static constexpr int KT = BCK * D;       // elements of the K tile
-  static constexpr int ST = BCK * BRQ;     // elements of a dS^T tile
 };
 
 // Asynchronous copy of query block [q0, q0 + BRQ) of Q and dO (natural row
-// order, swizzled chunks) and of its LSE*log2(e) and D rows into one stage.
-// Rows past N copy row N - 1 (their LSE is +inf, so they get P = 0).
+// order, qtile_swizzle chunks) and of its LSE*log2(e) and D rows into one
+// stage.  Rows past N copy row N - 1 (their LSE is +inf, so they get P = 0).
 template <int D>
 __device__ __forceinline__ void issue_q_tile(const uint16_t* Qh, const uint16_t* dOh,
                                              const float* lse2h, const float* delh,
                                              uint16_t* Qs, uint16_t* dOs, float* vec, int q0,
                                              int N, int w, int lane) {
-  using C = BwdCfg<D>;
+  using C = KvCfg<D>;
   constexpr int COPIES = C::BRQ * C::CPR / C::NT;
 #pragma unroll
   for (int t = 0; t < COPIES; ++t) {
     const int slot = (t * C::NW + w) * 64 + lane;
     const int row = slot / C::CPR;
-    const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
+    const int lc = (slot % C::CPR) ^ qtile_swizzle<D>(row);
     const int qq = min(q0 + row, N - 1);
     const int base = (t * C::NW + w) * 64 * 8;
     load_lds16(Qh + (int64_t)qq * D + lc * 8, Qs + base);
@@ -114,91 +99,80 @@ __device__ __forceinline__ void issue_q_tile(const uint16_t* Qh, const uint16_t*
   }
 }
 
-// Shared memory of the key-block pass: the K block (for the K^T operand of
-// dS K), double-buffered Q / dO tiles with their LSE*log2(e) and D rows, and
-// double-buffered dS^T tiles ([key][query], bf16).
-template <int D>
-struct BwdSmem {
-  using C = BwdCfg<D>;
-  uint16_t k[C::KT];
-  uint16_t q[2][C::QT];
-  uint16_t dout[2][C::QT];
-  uint16_t dst[2][C::ST];
-  float vec[2][2 * C::BRQ];
+// LDS of the key-block pass: double-buffered Q / dO tiles with their
+// LSE*log2(e) and D rows.  Every buffer is its own LDS object, so the
+// compiler can tell that the copies into one stage never overlap reads of
+// the other and does not wait for them.
+struct KvSmem {
+  uint16_t* q[2];
+  uint16_t* dout[2];
+  float* vec[2];
 };
 
-// One workgroup of the key-block pass: per-lane state and the steps of one
-// query block.  Stage indices are template parameters so every LDS offset
-// that does not depend on the lane is a compile-time immediate.
+// One workgroup of the key-block pass (8 waves, 16 keys each).  S = Q K^T,
+// dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS use v_mfma_f32_16x16x32_bf16
+// with a lane owning one key; the 16 queries of an S tile are fed in the
+// order that gives each lane 8 consecutive queries per 32-query group, so P
+// and dS are directly the B operands of the dV and dK products.
 template <int D, bool CAUSAL>
-struct BwdBlock {
-  using C = BwdCfg<D>;
+struct KvBlock {
+  using C = KvCfg<D>;
   static constexpr int BRQ = C::BRQ, BCK = C::BCK;
 
-  BwdSmem<D>& sm;
+  const KvSmem sm;
   const BwdArgs& a;
-  int w, lane, c32, g, N, bh, kb0, kw0, key, nqb;
+  int w, lane, c16, kg, N, kb0, kw0, key, nqb;
   int64_t hoff;
   const uint16_t* Qh;
   const uint16_t* dOh;
   const float* lse2h;
   const float* delh;
-  float* dQh;
   float sl2;
-  TrLane<D> trd;       // transposed reads of the Q, dO and K tiles
-  TrLane<BRQ> trs;     // transposed reads of the dS^T tile
-  RowLane<D> rowd;     // row reads of the Q and dO tiles
-  int dsw_base, dsw_u; // dS^T row writes
-  int kr_base, kr_u;   // row reads of this lane's key in the K block
-  bf16x8 vf[D / 16];
-  f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: lane holds [32 db + 8(i/4) + 4g + i%4][key]
+  int srow_base, srow_u;  // 16-byte row reads of Q / dO for S and dP
+  int tq_base, tq_t;      // transposed reads of Q / dO for dK and dV
+  bf16x8 kf[D / 32], vf[D / 32];  // B operands: K, V rows of this lane's key
+  f32x4 dk[D / 16], dv[D / 16];   // dK^T, dV^T: lane holds [16 dt + 4 kg + i][key]
 
-  __device__ __forceinline__ BwdBlock(BwdSmem<D>& sm_, const BwdArgs& a_, int bh_, int kb0_)
-      : sm(sm_), a(a_), trd(threadIdx.x & 63), trs(threadIdx.x & 63), rowd(threadIdx.x & 63) {
+  __device__ __forceinline__ KvBlock(const KvSmem& sm_, const BwdArgs& a_, int bh, int kb0_)
+      : sm(sm_), a(a_) {
     const int tid = threadIdx.x;
     w = tid >> 6;
     lane = tid & 63;
-    c32 = lane & 31;
-    g = lane >> 5;
+    c16 = lane & 15;
+    kg = lane >> 4;
     N = a.N;
-    bh = bh_;
     kb0 = kb0_;
     kw0 = kb0 + w * C::KW;
-    key = kw0 + c32;
+    key = kw0 + c16;
     nqb = (N + BRQ - 1) / BRQ;
     hoff = (int64_t)bh * N * D;
     Qh = a.q + hoff;
     dOh = a.dout + hoff;
     lse2h = a.lse2 + (int64_t)bh * a.Npad;
     delh = a.delta + (int64_t)bh * a.Npad;
-    dQh = a.dq_acc + hoff;
     sl2 = a.scale_log2;
-    dsw_base = (w * C::KW + c32) * BRQ;
-    dsw_u = g ^ chunk_swizzle<BRQ>(c32);
-    kr_base = (w * C::KW + c32) * D;
-    kr_u = g ^ chunk_swizzle<D>(c32);
-  }
-
-  __device__ __forceinline__ void issue_k_block() {
-    constexpr int COPIES = BCK * C::CPR / C::NT;
-#pragma unroll
-    for (int t = 0; t < COPIES; ++t) {
-      const int slot = (t * C::NW + w) * 64 + lane;
-      const int row = slot / C::CPR;
-      const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
-      const int kk = min(kb0 + row, N - 1);
-      load_lds16(a.k + hoff + (int64_t)kk * D + lc * 8, sm.k + (t * C::NW + w) * 64 * 8);
-    }
+    // row of S tile t in 32-query group qg fed by lane c16:
+    // 32 qg + 8 (c16 / 4) + 4 t + c16 % 4 (t and qg do not change the swizzle)
+    const int sr = 8 * (c16 >> 2) + (c16 & 3);
+    srow_base = sr * D;
+    srow_u = kg ^ qtile_swizzle<D>(sr);
+    // transposed reads: lane 16 G + 4 e + q reads row 32 qg + 8 G + e (+4),
+    // columns 16 dt + 4 q .. + 3
+    const int te = (lane >> 2) & 3, tq = lane & 3;
+    const int tr = 8 * kg + te;
+    tq_base = tr * D + 4 * (tq & 1);
+    tq_t = (tq >> 1) ^ qtile_swizzle<D>(tr);
   }
 
   __device__ __forceinline__ void load_kv_operands() {
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      const int64_t off = hoff + (int64_t)key * D + kc * 16 + g * 8;
-      vf[kc] = key < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
+    for (int s = 0; s < D / 32; ++s) {
+      const int64_t off = hoff + (int64_t)key * D + 32 * s + 8 * kg;
+      kf[s] = key < N ? load_global<bf16x8>(a.k + off) : zero_bf16x8();
+      vf[s] = key < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
     }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
+    for (int dt = 0; dt < D / 16; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
   }
 
   template <int ST>
@@ -206,211 +180,323 @@ struct BwdBlock {
     issue_q_tile<D>(Qh, dOh, lse2h, delh, sm.q[ST], sm.dout[ST], sm.vec[ST], i * BRQ, N, w, lane);
   }
 
-  // dQ rows of query block ib += dS K over the block's keys, from dS^T stage
-  // ST.  Wave w computes 32-column slices: db = w (d = 128) or
-  // (qs, db) = (w / 2, w % 2) (d = 64).
+  // S, P, dP, dS for query block i (stage ST); dV^T and dK^T accumulate.
   template <int ST>
-  __device__ __forceinline__ void dq_block(int ib) {
-    const uint16_t* sd = sm.dst[ST];
-    const TrLane<D> trd = this->trd.fresh();
-    const TrLane<BRQ> trs = this->trs.fresh();
-    constexpr int TASKS = (BRQ / 32) * (D / 32);
-#pragma unroll
-    for (int t0 = 0; t0 < TASKS; t0 += C::NW) {
-      const int t = t0 + w;
-      const int qs = t / (D / 32), db = t % (D / 32);
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int kc = 0; kc < BCK / 16; ++kc) {
-        const bf16x8 sa = join_tr(lds_read_tr(sd + trs.off(16 * kc, 32 * qs, 0)),
-                                  lds_read_tr(sd + trs.off(16 * kc, 32 * qs, 1)));
-        const bf16x8 kt = join_tr(lds_read_tr(sm.k + trd.off(16 * kc, 32 * db, 0)),
-                                  lds_read_tr(sm.k + trd.off(16 * kc, 32 * db, 1)));
-        acc = mfma32(sa, kt, acc);
-      }
-      // rows qb0 + 8 (idx/4) + 4 g + idx%4, column 32 db + c32
-      const int qb0 = ib * BRQ + 32 * qs;
-      float* base = dQh + (int64_t)(qb0 + 4 * g) * D + db * 32 + c32;
-      if (qb0 + 32 <= N) {
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx)
-          atomicAdd(base + (8 * (idx >> 2) + (idx & 3)) * D, acc[idx]);
-      } else {
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx)
-          if (qb0 + 4 * g + 8 * (idx >> 2) + (idx & 3) < N)
-            atomicAdd(base + (8 * (idx >> 2) + (idx & 3)) * D, acc[idx]);
-      }
-    }
-  }
-
-  // S, P, dP, dS for query block i (stage ST): dV^T, dK^T accumulate; dS^T
-  // goes to LDS stage ST for the dQ product.
-  template <int ST>
-  __device__ __forceinline__ void kv_block(int i) {
+  __device__ __forceinline__ void block(int i) {
     const uint16_t* Qt = sm.q[ST];
     const uint16_t* dOt = sm.dout[ST];
     const float* lv = sm.vec[ST];
-    uint16_t* sd = sm.dst[ST];
     const int q0 = i * BRQ;
-    const TrLane<D> trd = this->trd.fresh();
-    const RowLane<D> rowd = this->rowd.fresh();
-    const int kr_base = opaque(this->kr_base), kr_u = opaque(this->kr_u);
-    const int dsw_base = opaque(this->dsw_base), dsw_u = opaque(this->dsw_u);
+    const int sb = opaque(srow_base), su = opaque(srow_u);
+    const int tb = opaque(tq_base), tt = opaque(tq_t);
 #pragma unroll
-    for (int qs = 0; qs < BRQ / 32; ++qs) {
-      // value idx <-> query q0 + 32 qs + 16 (idx/8) + 8 g + idx%8, key `key`
-      const bool skip = CAUSAL && (kw0 > q0 + 32 * qs + 31);
-      float p[16], ds[16];
-      if (!skip) {
-        f32x16 s = zero16(), dp = zero16();
+    for (int qg = 0; qg < BRQ / 32; ++qg) {
+      // lane (key, kg) gets queries q0 + 32 qg + 8 kg + j, j < 8
+      if (CAUSAL && (kw0 > q0 + 32 * qg + 31)) continue;  // every key after every query
+      f32x4 s[2], dp[2];
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const int o = rowd.off(32 * qs, kc);
-          const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sm.k + kr_base + (((2 * kc) ^ kr_u) << 3));
-          s = mfma32(*reinterpret_cast<const bf16x8*>(Qt + o), kb, s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(dOt + o), vf[kc], dp);
+      for (int t = 0; t < 2; ++t) {
+        s[t] = zero4();
+        dp[t] = zero4();
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+          const int o = (32 * qg + 4 * t) * D + sb + (((4 * k) ^ su) << 3);
+          s[t] = mfma16(*reinterpret_cast<const bf16x8*>(Qt + o), kf[k], s[t]);
+          dp[t] = mfma16(*reinterpret_cast<const bf16x8*>(dOt + o), vf[k], dp[t]);
         }
-        const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qs);
+      }
+      const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qg);
+      const int ql = 32 * qg + 8 * kg;
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lv + ql);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lv + ql + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql + 4);
+      float p[8], ds[8];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int ql = 32 * qs + 16 * c + 8 * g;
-          const f32x4 l0 = *reinterpret_cast<const f32x4*>(lv + ql);
-          const f32x4 l1 = *reinterpret_cast<const f32x4*>(lv + ql + 4);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql + 4);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int idx = 8 * c + jj;
-            const float lse = jj < 4 ? l0[jj] : l1[jj - 4];
-            const float dlt = jj < 4 ? d0[jj] : d1[jj - 4];
-            float pv = exp2_fast(fmaf(s[idx], sl2, -lse));
-            if (need_mask) {
-              const int q = q0 + ql + jj;
-              if (key >= N || (CAUSAL && key > q)) pv = 0.f;
-            }
-            p[idx] = pv;
-            ds[idx] = pv * (dp[idx] - dlt);
-          }
+      for (int j = 0; j < 8; ++j) {
+        const float sv = j < 4 ? s[0][j] : s[1][j - 4];
+        const float dpv = j < 4 ? dp[0][j] : dp[1][j - 4];
+        const float lse = j < 4 ? l0[j] : l1[j - 4];
+        const float dlt = j < 4 ? d0[j] : d1[j - 4];
+        float pv = exp2_fast(fmaf(sv, sl2, -lse));
+        if (need_mask) {
+          const int q = q0 + ql + j;
+          if (key >= N || (CAUSAL && key > q)) pv = 0.f;
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over the sub-block's 32 queries.
+        p[j] = pv;
+        ds[j] = pv * (dpv - dlt);
+      }
+      const bf16x8 pb = pack8(p);
+      const bf16x8 sbv = pack8(ds);
+      // dV^T += dO^T P, dK^T += Q^T dS over the group's 32 queries; dO^T and
+      // Q^T come transposed out of the row-major tiles.
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 pb = pack8(p + 8 * c);
-          const bf16x8 sb = pack8(ds + 8 * c);
-          const int R0 = 32 * qs + 16 * c;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int o0 = trd.off(R0, 32 * db, 0), o1 = trd.off(R0, 32 * db, 1);
-            const bf16x8 oa = join_tr(lds_read_tr(dOt + o0), lds_read_tr(dOt + o1));
-            const bf16x8 qa = join_tr(lds_read_tr(Qt + o0), lds_read_tr(Qt + o1));
-            dv[db] = mfma32(oa, pb, dv[db]);
-            dk[db] = mfma32(qa, sb, dk[db]);
-          }
-          // dS^T row `key`, 8 consecutive queries (16 bytes)
-          *reinterpret_cast<bf16x8*>(sd + dsw_base + (((4 * qs + 2 * c) ^ dsw_u) << 3)) = sb;
-        }
-      } else {
-        const bf16x8 z = zero_bf16x8();
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          *reinterpret_cast<bf16x8*>(sd + dsw_base + (((4 * qs + 2 * c) ^ dsw_u) << 3)) = z;
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int o0 = (32 * qg) * D + tb + (((2 * dt) ^ tt) << 3);
+        const int o1 = o0 + 4 * D;
+        const bf16x8 oa = join_tr(lds_read_tr(dOt + o0), lds_read_tr(dOt + o1));
+        const bf16x8 qa = join_tr(lds_read_tr(Qt + o0), lds_read_tr(Qt + o1));
+        dv[dt] = mfma16(oa, pb, dv[dt]);
+        dk[dt] = mfma16(qa, sbv, dk[dt]);
       }
     }
   }
 
-  // One iteration of the steady state: prefetch block i + 1, dQ of block
-  // i - 1, then block i.
+  // Block i from stage ST, with block i + 1 prefetched into the other stage.
   template <int ST>
   __device__ __forceinline__ void step(int i) {
     if (i + 1 < nqb) issue_q<ST ^ 1>(i + 1);
-    dq_block<ST ^ 1>(i - 1);
-    kv_block<ST>(i);
+    block<ST>(i);
     wait_vmem();
     __syncthreads();
   }
 
-  __device__ __forceinline__ void store_dkdv() {
+  __device__ __forceinline__ void store() {
     if (key >= N) return;
     uint16_t* dKrow = a.dk + hoff + (int64_t)key * D;
     uint16_t* dVrow = a.dv + hoff + (int64_t)key * D;
     const float sc = a.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int col = db * 32 + 8 * r4 + 4 * g;
-        u32x2 kv, vv;
-        kv.x = pack2(dk[db][4 * r4 + 0] * sc, dk[db][4 * r4 + 1] * sc);
-        kv.y = pack2(dk[db][4 * r4 + 2] * sc, dk[db][4 * r4 + 3] * sc);
-        vv.x = pack2(dv[db][4 * r4 + 0], dv[db][4 * r4 + 1]);
-        vv.y = pack2(dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]);
-        *reinterpret_cast<u32x2*>(dKrow + col) = kv;
-        *reinterpret_cast<u32x2*>(dVrow + col) = vv;
-      }
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int col = 16 * dt + 4 * kg;
+      u32x2 kv, vv;
+      kv.x = pack2(dk[dt][0] * sc, dk[dt][1] * sc);
+      kv.y = pack2(dk[dt][2] * sc, dk[dt][3] * sc);
+      vv.x = pack2(dv[dt][0], dv[dt][1]);
+      vv.y = pack2(dv[dt][2], dv[dt][3]);
+      *reinterpret_cast<u32x2*>(dKrow + col) = kv;
+      *reinterpret_cast<u32x2*>(dVrow + col) = vv;
+    }
   }
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) fa_bwd_main_kernel(BwdArgs a) {
-  using C = BwdCfg<D>;
-  static_assert(C::BRQ == 64, "two 32-query sub-blocks per iteration");
-  __shared__ __attribute__((aligned(1024))) BwdSmem<D> sm;
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_bwd_kv_kernel(BwdArgs a) {
+  using C = KvCfg<D>;
+  static_assert(C::BRQ == 64, "two 32-query groups per iteration");
+  __shared__ __attribute__((aligned(1024))) uint16_t q0_s[C::QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t q1_s[C::QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t do0_s[C::QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t do1_s[C::QT];
+  __shared__ __attribute__((aligned(16))) float vec0_s[2 * C::BRQ];
+  __shared__ __attribute__((aligned(16))) float vec1_s[2 * C::BRQ];
+  const KvSmem sm{{q0_s, q1_s}, {do0_s, do1_s}, {vec0_s, vec1_s}};
 
   const int N = a.N;
   const int nkb = (N + C::BCK - 1) / C::BCK;
-  // Workgroup -> (head, key block), XCD-contiguous like the forward pass.
-  // Causal key blocks near the start see the most query blocks, so the
-  // natural order is already heaviest first.
+  // Workgroup -> (head, key block), XCD-contiguous (consecutive ids land on
+  // different XCDs, round robin over 8) so the key blocks of one head share
+  // that XCD's L2.  Causal key blocks near the start see the most query
+  // blocks, so the natural order is already heaviest first.
   const int total = gridDim.x;
   int L = blockIdx.x;
   if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
   const int bh = L / nkb;
   const int kb = L - bh * nkb;
 
-  BwdBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
+  KvBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
   const int nqb = blk.nqb;
   const int i0 = CAUSAL ? blk.kb0 / C::BRQ : 0;
-  blk.issue_k_block();
   blk.template issue_q<0>(i0);
   blk.load_kv_operands();
   wait_vmem();
   __syncthreads();
+  int i = i0;
+  for (; i + 1 < nqb; i += 2) {
+    blk.template step<0>(i);
+    blk.template step<1>(i + 1);
+  }
+  if (i < nqb) blk.template step<0>(i);
+  blk.store();
+}
 
-  // block i0 (stage 0) has no previous dQ to do
-  if (i0 + 1 < nqb) blk.template issue_q<1>(i0 + 1);
-  blk.template kv_block<0>(i0);
+// ------------------------------------------------------------------ query-block pass
+template <int D>
+struct QCfg {
+  static constexpr int NW = 4;                      // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int QW = 32;                     // query rows per wave
+  static constexpr int BR = NW * QW;                // query rows per workgroup
+  static constexpr int BC = 64;                     // keys per K/V tile
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BC * D;
+  static constexpr int COPIES = BC * CPR / NT;
+};
+
+// One workgroup of the query-block pass (4 waves, 32 query rows each), laid
+// out like the forward pass: a lane owns one query row, K and V tiles stream
+// through a double-buffered LDS, and per tile
+//   S^T = K Q^T, dP^T = V dO^T (32x32x16, K / V rows as A operands),
+//   P^T = exp2(scale log2(e) S^T - LSE log2(e)), dS^T = P^T o (dP^T - D),
+//   dQ^T += K^T dS^T (K^T read transposed from the K tile, dS^T straight
+//   from registers as the B operand).
+// dQ stays in registers and is written once.
+template <int D, bool CAUSAL>
+struct QBlock {
+  using C = QCfg<D>;
+  static constexpr int BC = C::BC;
+
+  uint16_t* ks[2];
+  uint16_t* vs[2];
+  const uint16_t* Kh;
+  const uint16_t* Vh;
+  int w, lane, c32, g, N, qw0, qrow, nt;
+  float sl2, lse2, dlt;
+  bf16x8 qf[D / 16], dof[D / 16];  // B operands: Q, dO rows of this lane's query
+  f32x16 dq[D / 32];                // dQ^T: lane holds dQ[qrow][32 db + 8(i/4) + 4g + i%4]
+  RowLane<D> rowk;                  // row reads of K / V (row swap23(c32) of each block)
+  TrLane<D> trk;                    // transposed reads of K
+
+  template <int ST>
+  __device__ __forceinline__ void issue(int j) {
+#pragma unroll
+    for (int t = 0; t < C::COPIES; ++t) {
+      const int slot = (t * C::NW + w) * 64 + lane;
+      const int row = slot / C::CPR;
+      const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
+      const int kk = min(j * BC + row, N - 1);
+      const int base = (t * C::NW + w) * 64 * 8;
+      load_lds16(Kh + (int64_t)kk * D + lc * 8, ks[ST] + base);
+      load_lds16(Vh + (int64_t)kk * D + lc * 8, vs[ST] + base);
+    }
+  }
+
+  template <int ST>
+  __device__ __forceinline__ void step(int j) {
+    if (j + 1 < nt) issue<ST ^ 1>(j + 1);
+    const uint16_t* Ks = ks[ST];
+    const uint16_t* Vs = vs[ST];
+    const int k0 = j * BC;
+    if (!(CAUSAL && (k0 > qw0 + C::QW - 1))) {
+      const RowLane<D> rk = rowk.fresh();
+      const TrLane<D> tr = trk.fresh();
+      // S^T, dP^T: value i of s[sb] is key k0 + 32 sb + 16 (i/8) + 8 g + i%8
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb) { s[sb] = zero16(); dp[sb] = zero16(); }
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc)
+#pragma unroll
+        for (int sb = 0; sb < BC / 32; ++sb) {
+          const int o = rk.off(32 * sb, kc);
+          s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + o), qf[kc], s[sb]);
+          dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + o), dof[kc], dp[sb]);
+        }
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = exp2_fast(fmaf(s[sb][i], sl2, -lse2));
+          if (need_mask) {
+            const int key = k0 + 32 * sb + 16 * (i >> 3) + 8 * g + (i & 7);
+            if (key >= N || (CAUSAL && key > qrow)) pv = 0.f;
+          }
+          s[sb][i] = pv * (dp[sb][i] - dlt);  // dS^T
+        }
+      // dQ^T += K^T dS^T over the tile's four 16-key chunks.
+#pragma unroll
+      for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
+        float t8[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) t8[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
+        const bf16x8 dsb = pack8(t8);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 ka = join_tr(lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 0)),
+                                    lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 1)));
+          dq[db] = mfma32(ka, dsb, dq[db]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_bwd_q_kernel(BwdArgs a) {
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const int nqb = (N + C::BR - 1) / C::BR;
+  // Workgroup -> (head, query block): XCD-contiguous, heaviest causal
+  // blocks first within a head (as in the forward pass).
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int bh = L / nqb;
+  int qb = L - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+
+  const int64_t hoff = (int64_t)bh * N * D;
+  QBlock<D, CAUSAL> f;
+  f.ks[0] = k0s;
+  f.ks[1] = k1s;
+  f.vs[0] = v0s;
+  f.vs[1] = v1s;
+  f.Kh = a.k + hoff;
+  f.Vh = a.v + hoff;
+  f.w = tid >> 6;
+  f.lane = tid & 63;
+  f.c32 = f.lane & 31;
+  f.g = f.lane >> 5;
+  f.N = N;
+  const int q0 = qb * C::BR;
+  f.qw0 = q0 + f.w * C::QW;
+  f.qrow = f.qw0 + f.c32;
+  f.nt = (N + C::BC - 1) / C::BC;
+  if (CAUSAL) f.nt = min(f.nt, (q0 + C::BR + C::BC - 1) / C::BC);
+  f.sl2 = a.scale_log2;
+  f.rowk = RowLane<D>(f.lane);
+  f.trk = TrLane<D>(f.lane);
+
+  f.template issue<0>(0);
+  const bool real = f.qrow < N;
+  const int64_t ro = hoff + (int64_t)f.qrow * D;
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    f.qf[kc] = real ? load_global<bf16x8>(a.q + ro + kc * 16 + f.g * 8) : zero_bf16x8();
+    f.dof[kc] = real ? load_global<bf16x8>(a.dout + ro + kc * 16 + f.g * 8) : zero_bf16x8();
+  }
+  const int64_t vrow = (int64_t)bh * a.Npad + f.qrow;
+  f.lse2 = real ? a.lse2[vrow] : INFINITY;  // padded rows get P = 0
+  f.dlt = real ? a.delta[vrow] : 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) f.dq[db] = zero16();
   wait_vmem();
   __syncthreads();
-  int i = i0 + 1;
-  for (; i + 1 < nqb; i += 2) {
-    blk.template step<1>(i);
-    blk.template step<0>(i + 1);
+
+  int j = 0;
+  for (; j + 1 < f.nt; j += 2) {
+    f.template step<0>(j);
+    f.template step<1>(j + 1);
   }
-  if (i < nqb) {
-    blk.template step<1>(i);
-    blk.template dq_block<1>(nqb - 1);
-  } else {
-    blk.template dq_block<0>(nqb - 1);
+  if (j < f.nt) f.template step<0>(j);
+
+  if (real) {
+    uint16_t* row = a.dq + ro;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 val;
+        val.x = pack2(f.dq[db][4 * r4 + 0] * sc, f.dq[db][4 * r4 + 1] * sc);
+        val.y = pack2(f.dq[db][4 * r4 + 2] * sc, f.dq[db][4 * r4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * r4 + 4 * f.g) = val;
+      }
   }
-  blk.store_dkdv();
 }
 
-// ------------------------------------------------------------------ dQ convert
-__global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a, int64_t n8) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n8) return;
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(a.dq_acc + t * 8);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(a.dq_acc + t * 8 + 4);
-  const float sc = a.scale;
-  u32x4 r;
-  r.x = pack2(x0.x * sc, x0.y * sc);
-  r.y = pack2(x0.z * sc, x0.w * sc);
-  r.z = pack2(x1.x * sc, x1.y * sc);
-  r.w = pack2(x1.z * sc, x1.w * sc);
-  *reinterpret_cast<u32x4*>(a.dq + t * 8) = r;
-}
-
+// ------------------------------------------------------------------ launchers
 template <int D>
 static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Npad;
@@ -421,10 +507,19 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_main_t(const BwdArgs& a, hipStream_t stream) {
-  using C = BwdCfg<D>;
+static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t stream) {
+  using C = KvCfg<D>;
   const int64_t nkb = (a.N + C::BCK - 1) / C::BCK;
-  hipLaunchKernelGGL((fa_bwd_main_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.BH)), dim3(C::NT), 0,
+  hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.BH)), dim3(C::NT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_q_t(const BwdArgs& a, hipStream_t stream) {
+  using C = QCfg<D>;
+  const int64_t nqb = (a.N + C::BR - 1) / C::BR;
+  hipLaunchKernelGGL((fa_bwd_q_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.BH)), dim3(C::NT), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -433,16 +528,14 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t stream) {
   return d == 64 ? launch_pre_t<64>(a, stream) : launch_pre_t<128>(a, stream);
 }
 
-hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_main_t<64, true>(a, stream) : launch_main_t<64, false>(a, stream);
-  return causal ? launch_main_t<128, true>(a, stream) : launch_main_t<128, false>(a, stream);
+hipError_t launch_bwd_kv(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_kv_t<64, true>(a, stream) : launch_kv_t<64, false>(a, stream);
+  return causal ? launch_kv_t<128, true>(a, stream) : launch_kv_t<128, false>(a, stream);
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t stream) {
-  const int64_t n8 = (int64_t)a.BH * a.N * d / 8;
-  hipLaunchKernelGGL(fa_bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a,
-                     n8);
-  return hipGetLastError();
+hipError_t launch_bwd_q(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_q_t<64, true>(a, stream) : launch_q_t<64, false>(a, stream);
+  return causal ? launch_q_t<128, true>(a, stream) : launch_q_t<128, false>(a, stream);
 }
 
 }  // namespace fa

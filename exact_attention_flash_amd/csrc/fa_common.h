@@ -187,6 +187,18 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 // has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector memory operations are still in
+// flight.  The counter retires operations in issue order, so this waits for
+// everything issued before the last N operations (used to wait for tile
+// copies without waiting for atomics issued after them).
+template <int N>
+__device__ __forceinline__ void wait_vmem_except_last() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Keep the compiler from moving memory operations across this point.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 // gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane 4e + q supplies the address of 4 consecutive 16-bit values;
 // lane i of the group receives element i % 4 of the run supplied by lane
@@ -296,5 +308,56 @@ struct RowLane {
     return r;
   }
 };
+
+}  // namespace fa
+
+namespace fa {
+
+// Instruction-group scheduling hints for a software-pipelined loop of STEPS
+// steps, each with R LDS reads feeding M MFMAs: the reads of the first AHEAD
+// steps go first, then every step's MFMAs are followed by the reads of the
+// step AHEAD later.  Applies to the scheduling region it is placed in.
+template <int STEPS, int R, int M, int AHEAD>
+__device__ __forceinline__ void sched_pipeline() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+#pragma unroll
+  for (int s = 0; s < AHEAD; ++s) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
+    if (s + AHEAD < STEPS) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+}
+
+}  // namespace fa
+
+namespace fa {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_bf16.  Lane l = 16 kg + c, c < 16, kg < 4:
+//   A (16 x 32): lane holds A[c][8 kg .. 8 kg + 7]
+//   B (32 x 16): lane holds B[8 kg .. 8 kg + 7][c]
+//   C (16 x 16): lane holds C[4 kg + i][c], i < 4
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// XOR swizzle of the 16-byte chunks of the backward pass's Q and dO tiles
+// ([query][D] bf16).  Linear over row bits 0..4; chosen (by an exhaustive
+// bank model) so that the two operand reads of these tiles are free of bank
+// conflicts: 16-byte row reads where the 16 lanes of a group take rows
+// 8a + 4t + b (a, b < 4), and transposed reads of rows 8G + e (G, e < 4).
+template <int D>
+__device__ __forceinline__ int qtile_swizzle(int row) {
+  constexpr int m0 = D == 128 ? 6 : 4, m1 = D == 128 ? 4 : 2, m3 = D == 128 ? 9 : 5, m4 = 1;
+  return ((row & 1) ? m0 : 0) ^ ((row & 2) ? m1 : 0) ^ ((row & 8) ? m3 : 0) ^
+         ((row & 16) ? m4 : 0);
+}
 
 }  // namespace fa

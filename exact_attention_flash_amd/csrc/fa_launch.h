@@ -33,7 +33,6 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;      // workspace: fp32 [B, H, N, d]
   float* delta;       // workspace: fp32 [B*H, Npad], rowsum(dO o O), 0 on padding
   float* lse2;        // workspace: fp32 [B*H, Npad], LSE * log2(e), +inf on padding
   int N;
@@ -47,9 +46,10 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // The three backward stages, each one kernel launch, for head dim d (64 or
-// 128): the row pass, the pass over key blocks, and the dQ conversion.
+// 128): the row pass, the pass over key blocks (dK, dV) and the pass over
+// query blocks (dQ).
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_kv(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_q(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -15,9 +15,11 @@
  * device memory; it stores O and, per row, LSE = m + ln l, the single
  * statistic the FlashAttention-2 forward keeps for the backward pass
  * ("FlashAttention 系列技术详解", section "具体优化策略").  The backward pass
- * recomputes the scores from LSE ("FlashAttention 的基本原理", section 2.4)
- * and accumulates dQ across key blocks with atomic adds in device memory
- * (CMU notes, section "为什么前向和反向的并行化策略不同").
+ * recomputes the scores from LSE ("FlashAttention 的基本原理", section 2.4).
+ * The CMU notes (section "为什么前向和反向的并行化策略不同") accumulate dQ
+ * across key blocks with atomic adds; on MI355X those fp32 atomics are the
+ * bottleneck, so here dQ has its own pass over query blocks (recomputing S
+ * and dP for its rows) and every result, dQ included, is deterministic.
  *
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major [B, H, N, d]: element (b, h, n, c) is at
@@ -86,11 +88,10 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
                    int causal, float softmax_scale, void* stream);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs for this shape: an fp32
- * dQ accumulator [B, H, N, d] and two fp32 row vectors [B*H, Npad] (the
- * rowsum(dO o O) term and LSE in base 2; Npad is N rounded up to a multiple
- * of 64), each section rounded up to 256 bytes.  Returns 0 for an empty
- * problem and for invalid sizes.
+ * Bytes of device workspace flash_attn_bwd needs for this shape: two fp32
+ * row vectors [B*H, Npad] (the rowsum(dO o O) term D and LSE in base 2; Npad
+ * is N rounded up to a multiple of 64), each rounded up to 256 bytes.
+ * Returns 0 for an empty problem and for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
@@ -105,11 +106,10 @@ size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d
  *                flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
  *                aligned, no initialisation needed, caller-owned; it must
  *                not overlap any other argument.
- * Three launches on `stream`: a row pass (D_i = sum_c dO_ic O_ic, LSE in
- * base 2, dQ accumulator cleared), the main pass over key blocks (dK, dV
- * in registers, dQ by fp32 atomic adds), and the dQ conversion to bf16.
- * dQ's rounding depends on the order of the atomic adds, so it may differ
- * in the last bits from run to run; dK and dV are deterministic.
+ * Three launches on `stream`: a row pass (D_i = sum_c dO_ic O_ic and LSE in
+ * base 2 into the workspace), a pass over key blocks (dK, dV accumulated in
+ * registers per key block) and a pass over query blocks (dQ accumulated in
+ * registers per query block).  No atomics: the results are deterministic.
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dout,
@@ -127,11 +127,13 @@ int flash_attn_bwd(const void* q, const void* k, const void* v,
  * carries the state from one stage to the next.
  *
  * flash_attn_bwd_preprocess: D_i = sum_c dO_ic O_ic and LSE * log2(e) into
- *   the workspace, dQ accumulator cleared.  Reads o, lse, dout.
+ *   the workspace.  Reads o, lse, dout.
  * flash_attn_bwd_kv_blocks: the pass over key blocks.  Reads q, k, v, dout
- *   and the workspace written by the preprocess stage; writes dk, dv and
- *   adds into the workspace's dQ accumulator.
- * flash_attn_bwd_convert_dq: dq = bf16(softmax_scale * dQ accumulator).
+ *   and the workspace; writes dk, dv.
+ * flash_attn_bwd_q_blocks: the pass over query blocks.  Reads q, k, v, dout
+ *   and the workspace; writes dq.  The two passes are independent of each
+ *   other and may run in either order (or on two streams) after the
+ *   preprocess stage.
  */
 int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout,
                               void* workspace, size_t workspace_bytes,
@@ -143,9 +145,11 @@ int flash_attn_bwd_kv_blocks(const void* q, const void* k, const void* v,
                              int64_t B, int64_t H, int64_t N, int64_t d,
                              int causal, float softmax_scale, void* stream);
 
-int flash_attn_bwd_convert_dq(void* workspace, size_t workspace_bytes, void* dq,
-                              int64_t B, int64_t H, int64_t N, int64_t d,
-                              float softmax_scale, void* stream);
+int flash_attn_bwd_q_blocks(const void* q, const void* k, const void* v,
+                            const void* dout, void* dq,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d,
+                            int causal, float softmax_scale, void* stream);
 
 /* Static, human-readable text for a status code ("unknown status" if none). */
 const char* flash_attn_status_string(int status);

@@ -36,7 +36,7 @@ def test_library_exports_header_symbols():
     assert names == sorted(["flash_attn_fwd", "flash_attn_bwd",
                             "flash_attn_bwd_workspace_bytes", "flash_attn_status_string",
                             "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
-                            "flash_attn_bwd_convert_dq"])
+                            "flash_attn_bwd_q_blocks"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -55,12 +55,10 @@ def test_status_strings():
 def test_workspace_bytes():
     lib = load_library()
     rows = 4 * 16 * 4096
-    want = (rows * 128 * 4 + 255) // 256 * 256 + 2 * ((rows * 4 + 255) // 256 * 256)
-    assert lib.flash_attn_bwd_workspace_bytes(4, 16, 4096, 128) == want
-    # row vectors are padded to whole 64-row query blocks per head
-    assert lib.flash_attn_bwd_workspace_bytes(1, 1, 1, 64) == 256 + 2 * 256
-    want = (3 * 100 * 128 * 4 + 255) // 256 * 256 + 2 * ((3 * 128 * 4 + 255) // 256 * 256)
-    assert lib.flash_attn_bwd_workspace_bytes(1, 3, 100, 128) == want
+    assert lib.flash_attn_bwd_workspace_bytes(4, 16, 4096, 128) == 2 * rows * 4
+    # two fp32 row vectors, padded to whole 64-row query blocks per head
+    assert lib.flash_attn_bwd_workspace_bytes(1, 1, 1, 64) == 2 * 256
+    assert lib.flash_attn_bwd_workspace_bytes(1, 3, 100, 128) == 2 * ((3 * 128 * 4 + 255) // 256 * 256)
     assert lib.flash_attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert lib.flash_attn_bwd_workspace_bytes(1, 1, 10, 96) == 0
     assert lib.flash_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
@@ -137,9 +135,12 @@ def test_bwd_stage_validation():
                                         1, 2, 16, 128, 1, 0.1, None) == ALIAS
     assert lib.flash_attn_bwd_kv_blocks(A, 2 * A, 3 * A, 6 * A, 8 * A, 9 * A, 10 * A, need,
                                         1, 2, 16, 128, 1, 0.0, None) == SCALE
-    assert lib.flash_attn_bwd_convert_dq(10 * A, need, 7 * A + 4, 1, 2, 16, 128, 0.1,
-                                         None) == MISAL
-    assert lib.flash_attn_bwd_convert_dq(10 * A, need, 7 * A, 0, 2, 16, 128, 0.1, None) == FA_OK
+    assert lib.flash_attn_bwd_q_blocks(A, 2 * A, 3 * A, 6 * A, 7 * A + 4, 10 * A, need,
+                                       1, 2, 16, 128, 1, 0.1, None) == MISAL
+    assert lib.flash_attn_bwd_q_blocks(A, 2 * A, 3 * A, 6 * A, A, 10 * A, need,
+                                       1, 2, 16, 128, 1, 0.1, None) == ALIAS
+    assert lib.flash_attn_bwd_q_blocks(A, 2 * A, 3 * A, 6 * A, 7 * A, 10 * A, need,
+                                       0, 2, 16, 128, 1, 0.1, None) == FA_OK
 
 
 @no_gpu
