@@ -16,7 +16,7 @@ library), and the dominant kernel's roofline uses the chip's published dense
 bf16 MFMA peak of 2.5 PFLOP/s.
 
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
-step (32 whole heads of 64, forward + backward) on this host's cores.
+step (40 whole heads of 64, forward + backward) on this host's cores.
 """
 
 from __future__ import annotations
@@ -43,8 +43,11 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", help="named workload (default c5: fwd+bwd)")
-    ap.add_argument("--cpu-heads", type=int, default=32,
+    ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the step the CPU oracle times (0 = skip cpu_baseline)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters); not timed")
     return ap.parse_args()
 
 
@@ -80,7 +83,9 @@ def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
                     if p.get("user_api") == "blas") or 1
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    heads = [(0, 0), (wl.B - 1, wl.H - 1), (wl.B // 2, wl.H // 2), (0, wl.H - 1)][:n_heads]
+    n_heads = min(n_heads, wl.B * wl.H)
+    stride = max(1, (wl.B * wl.H) // n_heads)
+    heads = [divmod(i * stride, wl.H) for i in range(n_heads)]
     t0 = time.perf_counter()
     for b, h in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
@@ -154,6 +159,12 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
+    if args.calib_copy_mb > 0:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=q.device).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
