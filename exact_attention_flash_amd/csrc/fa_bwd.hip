@@ -71,33 +71,52 @@ struct KvCfg {
   static constexpr int QT = BRQ * D;       // elements of a Q or dO tile
 };
 
-// Asynchronous copy of query block [q0, q0 + BRQ) of Q and dO (natural row
-// order, qtile_swizzle chunks) and of its LSE*log2(e) and D rows into one
-// stage.  Rows past N copy row N - 1 (their LSE is +inf, so they get P = 0).
+// Asynchronous copies of query block [q0, q0 + BRQ) of Q and dO (natural
+// row order, qtile_swizzle chunks) into one stage.  Copy t of thread
+// (w, lane) fills 16-byte slot (t * NW + w) * 64 + lane of a tile; its source
+// byte offset within the block is the same for every block and is computed
+// once.  Rows past N copy row N - 1 (their LSE is +inf, so they get P = 0).
 template <int D>
-__device__ __forceinline__ void issue_q_tile(const uint16_t* Qh, const uint16_t* dOh,
-                                             const float* lse2h, const float* delh,
-                                             uint16_t* Qs, uint16_t* dOs, float* vec, int q0,
-                                             int N, int w, int lane) {
+struct QTileCopy {
   using C = KvCfg<D>;
-  constexpr int COPIES = C::BRQ * C::CPR / C::NT;
+  static constexpr int COPIES = C::BRQ * C::CPR / C::NT;
+  uint32_t off[COPIES];
+
+  __device__ __forceinline__ static int slot_row(int t, int w, int lane) {
+    return ((t * C::NW + w) * 64 + lane) / C::CPR;
+  }
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int t = 0; t < COPIES; ++t) {
-    const int slot = (t * C::NW + w) * 64 + lane;
-    const int row = slot / C::CPR;
-    const int lc = (slot % C::CPR) ^ qtile_swizzle<D>(row);
-    const int qq = min(q0 + row, N - 1);
-    const int base = (t * C::NW + w) * 64 * 8;
-    load_lds16(Qh + (int64_t)qq * D + lc * 8, Qs + base);
-    load_lds16(dOh + (int64_t)qq * D + lc * 8, dOs + base);
+    for (int t = 0; t < COPIES; ++t) {
+      const int slot = (t * C::NW + w) * 64 + lane;
+      const int r = slot / C::CPR;
+      off[t] = 2 * (r * D + (((slot % C::CPR) ^ qtile_swizzle<D>(r)) << 3));
+    }
   }
-  // LSE*log2(e) then D: 2 x BRQ floats = BRQ / 2 lanes of 16 bytes (padded rows)
-  if (w == 0 && lane < C::BRQ / 2) {
-    const int half = C::BRQ / 4;  // lanes per vector
-    const float* src = lane < half ? lse2h + q0 + 4 * lane : delh + q0 + 4 * (lane - half);
-    load_lds16(src, vec);
+  __device__ __forceinline__ void issue(const uint16_t* Qh, const uint16_t* dOh, uint16_t* Qs,
+                                        uint16_t* dOs, int q0, int N, int w, int lane) const {
+    constexpr uint32_t kBytes = C::BRQ * D * 2;
+    const buf_rsrc qr = make_rsrc(Qh + (int64_t)q0 * D, kBytes);
+    const buf_rsrc dr = make_rsrc(dOh + (int64_t)q0 * D, kBytes);
+    if (q0 + C::BRQ <= N) {
+#pragma unroll
+      for (int t = 0; t < COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        buffer_load_lds16(qr, off[t], Qs + base);
+        buffer_load_lds16(dr, off[t], dOs + base);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        const int r = slot_row(t, w, lane);
+        const int shift = (min(q0 + r, N - 1) - (q0 + r)) * D * 2;
+        buffer_load_lds16(qr, off[t] + shift, Qs + base);
+        buffer_load_lds16(dr, off[t] + shift, dOs + base);
+      }
+    }
   }
-}
+};
 
 // LDS of the key-block pass: double-buffered Q / dO tiles with their
 // LSE*log2(e) and D rows.  Every buffer is its own LDS object, so the
@@ -130,13 +149,14 @@ struct KvBlock {
   float sl2;
   int srow_base, srow_u;  // 16-byte row reads of Q / dO for S and dP
   int tq_base, tq_t;      // transposed reads of Q / dO for dK and dV
+  QTileCopy<D> cp;                // source offsets of the Q / dO tile copies
   bf16x8 kf[D / 32], vf[D / 32];  // B operands: K, V rows of this lane's key
   f32x4 dk[D / 16], dv[D / 16];   // dK^T, dV^T: lane holds [16 dt + 4 kg + i][key]
 
   __device__ __forceinline__ KvBlock(const KvSmem& sm_, const BwdArgs& a_, int bh, int kb0_)
       : sm(sm_), a(a_) {
     const int tid = threadIdx.x;
-    w = tid >> 6;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     lane = tid & 63;
     c16 = lane & 15;
     kg = lane >> 4;
@@ -162,6 +182,7 @@ struct KvBlock {
     const int tr = 8 * kg + te;
     tq_base = tr * D + 4 * (tq & 1);
     tq_t = (tq >> 1) ^ qtile_swizzle<D>(tr);
+    cp.init(w, lane);
   }
 
   __device__ __forceinline__ void load_kv_operands() {
@@ -177,7 +198,15 @@ struct KvBlock {
 
   template <int ST>
   __device__ __forceinline__ void issue_q(int i) {
-    issue_q_tile<D>(Qh, dOh, lse2h, delh, sm.q[ST], sm.dout[ST], sm.vec[ST], i * BRQ, N, w, lane);
+    const int q0 = i * BRQ;
+    cp.issue(Qh, dOh, sm.q[ST], sm.dout[ST], q0, N, w, lane);
+    // LSE*log2(e) then D of the block: 2 x BRQ floats = BRQ / 2 lanes of 16
+    // bytes (the rows are padded to whole blocks)
+    if (w == 0 && lane < BRQ / 2) {
+      constexpr int half = BRQ / 4;  // lanes per vector
+      const float* src = lane < half ? lse2h + q0 + 4 * lane : delh + q0 + 4 * (lane - half);
+      load_lds16(src, sm.vec[ST]);
+    }
   }
 
   // S, P, dP, dS for query block i (stage ST); dV^T and dK^T accumulate.
@@ -205,6 +234,8 @@ struct KvBlock {
           dp[t] = mfma16(*reinterpret_cast<const bf16x8*>(dOt + o), vf[k], dp[t]);
         }
       }
+      // keep the Q / dO reads two slices ahead of the MFMAs that consume them
+      sched_pipeline<2 * (D / 32), 2, 2, 2>();
       const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qg);
       const int ql = 32 * qg + 8 * kg;
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(lv + ql);
@@ -347,18 +378,46 @@ struct QBlock {
   f32x16 dq[D / 32];                // dQ^T: lane holds dQ[qrow][32 db + 8(i/4) + 4g + i%4]
   RowLane<D> rowk;                  // row reads of K / V (row swap23(c32) of each block)
   TrLane<D> trk;                    // transposed reads of K
+  uint32_t coff[C::COPIES];         // source offsets of the K / V tile copies
 
-  template <int ST>
-  __device__ __forceinline__ void issue(int j) {
+  // Copy t of thread (w, lane) fills 16-byte slot (t * NW + w) * 64 + lane of
+  // a K / V tile (natural row order, chunk_swizzle chunks); its source byte
+  // offset within the tile is the same for every tile.  Rows past N copy row
+  // N - 1 (finite data for keys that are masked anyway).
+  __device__ __forceinline__ static int slot_row(int t, int w, int lane) {
+    return ((t * C::NW + w) * 64 + lane) / C::CPR;
+  }
+  __device__ __forceinline__ void init_copies() {
 #pragma unroll
     for (int t = 0; t < C::COPIES; ++t) {
       const int slot = (t * C::NW + w) * 64 + lane;
-      const int row = slot / C::CPR;
-      const int lc = (slot % C::CPR) ^ chunk_swizzle<D>(row);
-      const int kk = min(j * BC + row, N - 1);
-      const int base = (t * C::NW + w) * 64 * 8;
-      load_lds16(Kh + (int64_t)kk * D + lc * 8, ks[ST] + base);
-      load_lds16(Vh + (int64_t)kk * D + lc * 8, vs[ST] + base);
+      const int r = slot / C::CPR;
+      coff[t] = 2 * (r * D + (((slot % C::CPR) ^ chunk_swizzle<D>(r)) << 3));
+    }
+  }
+
+  template <int ST>
+  __device__ __forceinline__ void issue(int j) {
+    constexpr uint32_t kBytes = BC * D * 2;
+    const int k0 = j * BC;
+    const buf_rsrc kr = make_rsrc(Kh + (int64_t)k0 * D, kBytes);
+    const buf_rsrc vr = make_rsrc(Vh + (int64_t)k0 * D, kBytes);
+    if (k0 + BC <= N) {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        buffer_load_lds16(kr, coff[t], ks[ST] + base);
+        buffer_load_lds16(vr, coff[t], vs[ST] + base);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        const int r = slot_row(t, w, lane);
+        const int shift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
+        buffer_load_lds16(kr, coff[t] + shift, ks[ST] + base);
+        buffer_load_lds16(vr, coff[t] + shift, vs[ST] + base);
+      }
     }
   }
 
@@ -383,6 +442,8 @@ struct QBlock {
           s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + o), qf[kc], s[sb]);
           dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + o), dof[kc], dp[sb]);
         }
+      // keep the K / V reads two slices ahead of the MFMAs that consume them
+      sched_pipeline<D / 16, 2 * (BC / 32), 2 * (BC / 32), 2>();
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
@@ -444,7 +505,7 @@ fa_bwd_q_kernel(BwdArgs a) {
   f.vs[1] = v1s;
   f.Kh = a.k + hoff;
   f.Vh = a.v + hoff;
-  f.w = tid >> 6;
+  f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   f.lane = tid & 63;
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
@@ -457,6 +518,7 @@ fa_bwd_q_kernel(BwdArgs a) {
   f.sl2 = a.scale_log2;
   f.rowk = RowLane<D>(f.lane);
   f.trk = TrLane<D>(f.lane);
+  f.init_copies();
 
   f.template issue<0>(0);
   const bool real = f.qrow < N;

@@ -22,9 +22,10 @@
 //    v_mfma_f32_32x32x16_bf16, so a lane owns one query and 32 of the tile's
 //    keys: the row max is an in-lane max plus one swap of wave halves, and the
 //    row sum needs no cross-lane step until the end;
-//  * K rows sit in LDS in swap23 order, which makes each lane's 16 scores per
-//    32-key block come out as two runs of eight consecutive keys: rounded to
-//    bf16 they are directly the B operand of O^T += V^T P^T;
+//  * K rows sit in LDS in swap23 order (bits 2 and 3 of the row swapped),
+//    which makes each lane's 16 scores per 32-key block come out as two runs
+//    of eight consecutive keys: rounded to bf16 they are directly the B
+//    operand of O^T += V^T P^T;
 //  * the V^T operand of that product is read from the row-major V tile with
 //    the transposing LDS read (ds_read_b64_tr_b16);
 //  * exponentials are base 2 with log2(e) folded into the scale, and the
@@ -55,28 +56,61 @@ struct FwdCfg {
 // running max is moved.
 constexpr float kRescaleThreshold = 8.f;
 
-// Issue the asynchronous copies of key tile [k0, k0 + BC) of K and V into
-// one LDS stage.  K row r of the tile holds key k0 + swap23(r); V row r holds
-// key k0 + r.  Rows past the end of the sequence copy the last valid row
-// (finite data; those keys are masked, so they contribute nothing).
+// Per-lane source offsets of the asynchronous tile copies.  Copy t of a lane
+// fills 16-byte slot (t * NW + w) * 64 + lane of a tile: row r = slot / CPR,
+// physical chunk slot % CPR, which holds logical chunk pc ^ swizzle(r).  V row
+// r is key r of the tile; K row r is key swap23(r), so that lane c of the
+// S^T product reads LDS row c (conflict-free) and still gets key swap23(c).
+// The offsets are the same for every tile and are computed once; a tile
+// that runs past the end of the sequence clamps its keys to N - 1 (finite
+// data for keys that are masked anyway).
 template <int D>
-__device__ __forceinline__ void issue_kv_tile(const uint16_t* Kh, const uint16_t* Vh,
-                                              uint16_t* Ks, uint16_t* Vs, int k0, int N,
-                                              int w, int lane) {
+struct TileCopy {
   using C = FwdCfg<D>;
-#pragma unroll
-  for (int t = 0; t < C::COPIES; ++t) {
-    const int slot = (t * C::NW + w) * 64 + lane;  // 16-byte slot in the tile
-    const int row = slot / C::CPR;
-    const int pc = slot % C::CPR;                  // physical chunk
-    const int lc = pc ^ chunk_swizzle<D>(row);     // logical chunk it holds
-    const int kk = min(k0 + swap23(row), N - 1);
-    const int vk = min(k0 + row, N - 1);
-    const int wave_base = (t * C::NW + w) * 64 * 8;  // elements
-    load_lds16(Kh + (int64_t)kk * D + lc * 8, Ks + wave_base);
-    load_lds16(Vh + (int64_t)vk * D + lc * 8, Vs + wave_base);
+  uint32_t koff[C::COPIES];  // byte offsets of the lane's 16 bytes in K and V
+  uint32_t voff[C::COPIES];
+
+  __device__ __forceinline__ static int slot_row(int t, int w, int lane) {
+    return ((t * C::NW + w) * 64 + lane) / C::CPR;
   }
-}
+
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int t = 0; t < C::COPIES; ++t) {
+      const int slot = (t * C::NW + w) * 64 + lane;
+      const int r = slot / C::CPR;
+      const int chunk = ((slot % C::CPR) ^ chunk_swizzle<D>(r)) << 3;
+      koff[t] = 2 * (swap23(r) * D + chunk);
+      voff[t] = 2 * (r * D + chunk);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint16_t* Kh, const uint16_t* Vh, uint16_t* Ks,
+                                        uint16_t* Vs, int k0, int N, int w, int lane) const {
+    constexpr uint32_t kTileBytes = C::BC * D * 2;
+    const buf_rsrc kr = make_rsrc(Kh + (int64_t)k0 * D, kTileBytes);
+    const buf_rsrc vr = make_rsrc(Vh + (int64_t)k0 * D, kTileBytes);
+    if (k0 + C::BC <= N) {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        buffer_load_lds16(kr, koff[t], Ks + base);
+        buffer_load_lds16(vr, voff[t], Vs + base);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t) {
+        const int base = (t * C::NW + w) * 64 * 8;
+        const int r = slot_row(t, w, lane);
+        const int kr_row = swap23(r);
+        const int kshift = (min(k0 + kr_row, N - 1) - (k0 + kr_row)) * D * 2;
+        const int vshift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
+        buffer_load_lds16(kr, koff[t] + kshift, Ks + base);
+        buffer_load_lds16(vr, voff[t] + vshift, Vs + base);
+      }
+    }
+  }
+};
 
 // LDS of one forward workgroup: K and V tiles of two stages, each its own
 // object.  Separate objects let the compiler see that the copies into one
@@ -106,6 +140,7 @@ struct FwdBlock {
   f32x16 oacc[D / 32];  // O^T: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
   TrLane<D> trv;        // transposed reads of the V tile
   int kbase, ku;        // row reads of the K tile (row c32 of each 32-key block)
+  TileCopy<D> cp;       // per-lane offsets of the tile copies
 
   template <int ST>
   __device__ __forceinline__ uint16_t* ktile() const { return ST ? sm.k1 : sm.k0; }
@@ -114,7 +149,7 @@ struct FwdBlock {
 
   template <int ST>
   __device__ __forceinline__ void issue(int j) {
-    issue_kv_tile<D>(Kh, Vh, ktile<ST>(), vtile<ST>(), j * BC, N, w, lane);
+    cp.issue(Kh, Vh, ktile<ST>(), vtile<ST>(), j * BC, N, w, lane);
   }
 
   // One key tile from stage ST; prefetches tile j + 1 into the other stage.
@@ -141,6 +176,8 @@ struct FwdBlock {
               *reinterpret_cast<const bf16x8*>(Ks + sb * 32 * D + kb + (((2 * kc) ^ kx) << 3));
           s[sb] = mfma32(ka, qf[kc], s[sb]);
         }
+      // keep the K reads two slices ahead of the MFMAs that consume them
+      sched_pipeline<D / 16, BC / 32, BC / 32, 2>();
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
       if (need_mask) {
 #pragma unroll
@@ -233,7 +270,7 @@ fa_fwd_kernel(FwdArgs a) {
   f.sm = FwdSmem<D>{k0s, v0s, k1s, v1s};
   f.Kh = a.k + hoff;
   f.Vh = a.v + hoff;
-  f.w = tid >> 6;
+  f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   f.lane = tid & 63;
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
@@ -249,6 +286,7 @@ fa_fwd_kernel(FwdArgs a) {
   f.trv = TrLane<D>(f.lane);
   f.kbase = f.c32 * D;
   f.ku = f.g ^ chunk_swizzle<D>(f.c32);
+  f.cp.init(f.w, f.lane);
 
   f.template issue<0>(0);
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
