@@ -68,6 +68,28 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max(x[lane], x[lane ^ 32]) and x[lane] + x[lane ^ 32] with one
+// v_permlane32_swap (gfx950): swapping one wave half of x against the other
+// leaves the two values of each lane pair in the two results.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup barrier without a memory fence: unlike __syncthreads() it does
+// not wait for this wave's outstanding global -> LDS copies.  The compiler
+// may not move memory operations across it.  Callers wait for the copies a
+// barrier must cover themselves (wait_vmem*).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T load_global(const void* p) {
   return *reinterpret_cast<const T*>(p);
@@ -200,17 +222,59 @@ __device__ __forceinline__ void buffer_load_lds16(buf_rsrc r, uint32_t voff, voi
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, 0, 0, 0);
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only:
+// vmcnt in bits 3:0 and 15:14, expcnt (bits 6:4) and lgkmcnt (bits 11:8)
+// left at their maximum.
+constexpr int waitcnt_vm_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | 0x70 | 0xF00; }
+
+// Buffer resource as four 32-bit words for inline assembly: base address
+// (48 bits, stride 0), size in bytes, gfx9 data-format word.  `base` must be
+// wave-uniform.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// The copy of buffer_load_lds16, issued from inline assembly so that the
+// compiler neither sees the LDS write nor adds waits for it: the caller
+// orders every read of the destination after the copy with its own
+// wait_vmem* and block_barrier.  The instruction has no register result;
+// its VGPR offset, resource and M0 (the LDS destination of lane 0) are read
+// when it issues.  M0 is declared clobbered.
+__device__ __forceinline__ void buffer_load_lds16_unseen(const i32x4& r, uint32_t voff,
+                                                         const void* lds_wave_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds), "s"(r)
+               : "memory", "m0");
+}
+
 // Wait until every global load (including global -> LDS copies) of this wave
-// has completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// has completed.  Issued through the builtin, so the compiler's own waitcnt
+// bookkeeping sees it and does not add a second, later wait.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_imm(0));
+  asm volatile("" ::: "memory");
+}
 
 // Wait until at most N of this wave's vector memory operations are still in
 // flight.  The counter retires operations in issue order, so this waits for
-// everything issued before the last N operations (used to wait for tile
-// copies without waiting for atomics issued after them).
+// everything issued before the last N operations (used to wait for older
+// tile copies while the newest ones stay in flight).
 template <int N>
 __device__ __forceinline__ void wait_vmem_except_last() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_imm(N));
+  asm volatile("" ::: "memory");
 }
 
 // Keep the compiler from moving memory operations across this point.

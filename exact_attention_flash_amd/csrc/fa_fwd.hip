@@ -11,13 +11,21 @@
 // a workgroup, over query rows per wave, so no two waves ever combine partial
 // results (CMU notes, section "并行化策略").
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows; K/V tiles of 64
-// keys; two workgroups per CU):
-//  * K and V tiles go global -> LDS with asynchronous 16-byte copies
-//    (global_load_lds_dwordx4) into a double buffer: the next tile is in
-//    flight while the current one is used, and no register holds staging
-//    data.  Tiles are unpadded row-major with an XOR swizzle of the 16-byte
-//    chunks, so that operand reads are free of bank conflicts;
+// gfx950 mapping (one workgroup = 8 waves = 256 query rows, 32 per wave; K/V
+// tiles of 64 keys; one workgroup per CU, two waves per SIMD):
+//  * ping-pong: waves w and w + 4 share a SIMD.  Each wave alternates a
+//    matrix phase (S^T = K Q^T for tile t and O^T += V^T P^T for tile t - 1,
+//    all MFMA and LDS reads) with a softmax phase (mask, row max, exp2, row
+//    sum, bf16 packing: all VALU) for tile t.  Waves 0-3 and 4-7 run these
+//    phases half a period apart, separated by workgroup barriers, so on each
+//    SIMD one wave keeps the matrix core busy while the other does the
+//    softmax arithmetic.  Measured on gfx950, an MFMA-only wave and a
+//    VALU-only wave on one SIMD overlap almost completely; two waves that
+//    each mix both kinds of work do not;
+//  * K and V tiles go global -> LDS with asynchronous 16-byte buffer loads
+//    into three buffers each: tile t + 2 of K and t + 1 of V are in flight
+//    while tile t is used.  Tiles are unpadded row-major with an XOR swizzle
+//    of the 16-byte chunks, so that operand reads are free of bank conflicts;
 //  * each wave computes S^T = K Q^T for its 32 queries with
 //    v_mfma_f32_32x32x16_bf16, so a lane owns one query and 32 of the tile's
 //    keys: the row max is an in-lane max plus one swap of wave halves, and the
@@ -42,7 +50,7 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = 4;                      // waves per workgroup
+  static constexpr int NW = 8;                      // waves per workgroup
   static constexpr int NT = NW * 64;                // threads per workgroup
   static constexpr int QW = 32;                     // query rows per wave
   static constexpr int BR = NW * QW;                // query rows per workgroup
@@ -50,6 +58,7 @@ struct FwdCfg {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int TILE = BC * D;               // elements per K or V tile
   static constexpr int COPIES = BC * CPR / NT;      // 16-byte copies per thread per tile
+  static_assert(COPIES >= 1 && COPIES * NT == BC * CPR, "tile copies must split evenly");
 };
 
 // Largest growth of the probabilities (in log2 units) tolerated before the
@@ -60,10 +69,10 @@ constexpr float kRescaleThreshold = 8.f;
 // fills 16-byte slot (t * NW + w) * 64 + lane of a tile: row r = slot / CPR,
 // physical chunk slot % CPR, which holds logical chunk pc ^ swizzle(r).  V row
 // r is key r of the tile; K row r is key swap23(r), so that lane c of the
-// S^T product reads LDS row c (conflict-free) and still gets key swap23(c).
-// The offsets are the same for every tile and are computed once; a tile
-// that runs past the end of the sequence clamps its keys to N - 1 (finite
-// data for keys that are masked anyway).
+// S^T product reads LDS row c and still gets key swap23(c).  The offsets are
+// the same for every tile and are computed once; a tile that runs past the
+// end of the sequence clamps its keys to N - 1 (finite data for keys that are
+// masked anyway).
 template <int D>
 struct TileCopy {
   using C = FwdCfg<D>;
@@ -85,201 +94,258 @@ struct TileCopy {
     }
   }
 
-  __device__ __forceinline__ void issue(const uint16_t* Kh, const uint16_t* Vh, uint16_t* Ks,
-                                        uint16_t* Vs, int k0, int N, int w, int lane) const {
-    constexpr uint32_t kTileBytes = C::BC * D * 2;
-    const buf_rsrc kr = make_rsrc(Kh + (int64_t)k0 * D, kTileBytes);
-    const buf_rsrc vr = make_rsrc(Vh + (int64_t)k0 * D, kTileBytes);
+  // One tile (rows k0 .. k0 + BC - 1) of K (KEYS) or V (!KEYS) into Ts.
+  template <bool KEYS>
+  __device__ __forceinline__ void issue(const uint16_t* Xh, uint16_t* Ts, int k0, int N, int w,
+                                        int lane) const {
+    const i32x4 rs = make_rsrc_words(Xh + (int64_t)k0 * D, C::BC * D * 2);
     if (k0 + C::BC <= N) {
 #pragma unroll
-      for (int t = 0; t < C::COPIES; ++t) {
-        const int base = (t * C::NW + w) * 64 * 8;
-        buffer_load_lds16(kr, koff[t], Ks + base);
-        buffer_load_lds16(vr, voff[t], Vs + base);
-      }
+      for (int t = 0; t < C::COPIES; ++t)
+        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + (t * C::NW + w) * 64 * 8);
     } else {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t) {
-        const int base = (t * C::NW + w) * 64 * 8;
-        const int r = slot_row(t, w, lane);
-        const int kr_row = swap23(r);
-        const int kshift = (min(k0 + kr_row, N - 1) - (k0 + kr_row)) * D * 2;
-        const int vshift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
-        buffer_load_lds16(kr, koff[t] + kshift, Ks + base);
-        buffer_load_lds16(vr, voff[t] + vshift, Vs + base);
+        const int r = KEYS ? swap23(slot_row(t, w, lane)) : slot_row(t, w, lane);
+        const int shift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
+        buffer_load_lds16_unseen(rs, (KEYS ? koff[t] : voff[t]) + shift,
+                                 Ts + (t * C::NW + w) * 64 * 8);
       }
     }
   }
 };
 
-// LDS of one forward workgroup: K and V tiles of two stages, each its own
-// object.  Separate objects let the compiler see that the copies into one
-// stage never overlap reads of the other, so it does not wait for the
-// in-flight copies before reading the current tile.
-template <int D>
+// LDS of one forward workgroup: three K and three V tile buffers.  The tile
+// copies are invisible to the compiler; the period structure orders every
+// read of a buffer after the wait and barrier that follow its copy.
 struct FwdSmem {
-  uint16_t* k0;
-  uint16_t* v0;
-  uint16_t* k1;
-  uint16_t* v1;
+  uint16_t* k[3];
+  uint16_t* v[3];
 };
 
 template <int D, bool CAUSAL>
-struct FwdBlock {
+struct FwdWave {
   using C = FwdCfg<D>;
   static constexpr int BC = C::BC;
 
-  FwdSmem<D> sm;
+  FwdSmem sm;
   const uint16_t* Kh;
   const uint16_t* Vh;
-  int w, lane, c32, g, N, qw0, qrow, nt;
+  int w, grp, lane, c32, g, N, qw0, qrow, nt, ntw;
   float sl2;
   float m_run;   // running max of scale*log2(e)*s (possibly stale)
   float l_part;  // this lane's share of the running row sum
   bf16x8 qf[D / 16];
   f32x16 oacc[D / 32];  // O^T: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
+  f32x16 s[BC / 32];    // S^T of the tile between the matrix and softmax phases
+  bf16x8 pb[BC / 16];   // P^T of the tile between the softmax and matrix phases
   TrLane<D> trv;        // transposed reads of the V tile
   int kbase, ku;        // row reads of the K tile (row c32 of each 32-key block)
   TileCopy<D> cp;       // per-lane offsets of the tile copies
 
-  template <int ST>
-  __device__ __forceinline__ uint16_t* ktile() const { return ST ? sm.k1 : sm.k0; }
-  template <int ST>
-  __device__ __forceinline__ uint16_t* vtile() const { return ST ? sm.v1 : sm.v0; }
-
-  template <int ST>
-  __device__ __forceinline__ void issue(int j) {
-    cp.issue(Kh, Vh, ktile<ST>(), vtile<ST>(), j * BC, N, w, lane);
+  // S^T = K Q^T for the tile in K buffer KB.  Value i of s[sb] is the score
+  // of key 32 sb + 16 (i / 8) + 8 g + i % 8 of the tile against qrow.
+  template <int KB>
+  __device__ __forceinline__ void scores() {
+    const uint16_t* Ks = sm.k[KB];
+    const int kb = opaque(kbase), kx = opaque(ku);
+#pragma unroll
+    for (int sb = 0; sb < BC / 32; ++sb) s[sb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+#pragma unroll
+      for (int sb = 0; sb < BC / 32; ++sb) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(Ks + sb * 32 * D + kb + (((2 * kc) ^ kx) << 3));
+        s[sb] = mfma32(ka, qf[kc], s[sb]);
+      }
+    // keep the K reads two contraction slices ahead of the MFMAs using them
+    sched_pipeline<D / 16, BC / 32, BC / 32, 2>();
   }
 
-  // One key tile from stage ST; prefetches tile j + 1 into the other stage.
-  template <int ST>
-  __device__ __forceinline__ void step(int j) {
-    if (j + 1 < nt) issue<ST ^ 1>(j + 1);
-    const uint16_t* Ks = ktile<ST>();
-    const uint16_t* Vs = vtile<ST>();
-    const int k0 = j * BC;
-    const bool skip = CAUSAL && (k0 > qw0 + C::QW - 1);
-    if (!skip) {
-      const TrLane<D> tr = trv.fresh();
-      const int kb = opaque(kbase), kx = opaque(ku);
-      // S^T for the tile: two 32-key blocks.  Value i of s[sb] is the score
-      // of key k0 + 32 sb + 16 (i / 8) + 8 g + i % 8 against qrow.
-      f32x16 s[BC / 32];
+  // O^T += V^T P^T for the tile in V buffer VB over its four 16-key chunks.
+  // B operand: P^T chunk kc2 (keys 16 kc2 + 8 g + 0..7 of this lane's query).
+  // A operand: V^T rows 32 db + c32, read transposed from the V tile.
+  template <int VB>
+  __device__ __forceinline__ void pv() {
+    const uint16_t* Vs = sm.v[VB];
+    const TrLane<D> tr = trv.fresh();
 #pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb) s[sb] = zero16();
+    for (int kc2 = 0; kc2 < BC / 16; ++kc2)
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc)
-#pragma unroll
-        for (int sb = 0; sb < BC / 32; ++sb) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(Ks + sb * 32 * D + kb + (((2 * kc) ^ kx) << 3));
-          s[sb] = mfma32(ka, qf[kc], s[sb]);
-        }
-      // keep the K reads two slices ahead of the MFMAs that consume them
-      sched_pipeline<D / 16, BC / 32, BC / 32, 2>();
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
-      if (need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < BC / 32; ++sb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * sb + 16 * (i >> 3) + 8 * g + (i & 7);
-            if (key >= N || (CAUSAL && key > qrow)) s[sb][i] = -INFINITY;
-          }
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 va = join_tr(lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 0)),
+                                  lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 1)));
+        oacc[db] = mfma32(va, pb[kc2], oacc[db]);
       }
-      float mx = -INFINITY;
+    // keep the V reads one 16-key chunk ahead of the MFMAs using them
+    sched_pipeline<BC / 16, 2 * (D / 32), D / 32, 1>();
+  }
+
+  // Matrix phase of period t: S^T of tile t (K buffer KB) and O^T += V^T P^T
+  // of tile t - 1 (V buffer VB), each only where this wave has that tile.
+  template <int KB, int VB>
+  __device__ __forceinline__ void matrix_phase(int t) {
+    const bool do_s = t < ntw;
+    const bool do_pv = t >= 1 && t - 1 < ntw;
+    if (do_s) scores<KB>();
+    if (do_pv) pv<VB>();
+  }
+
+  // Softmax phase for tile t: P^T = exp2(scale log2(e) S^T - m) into pb,
+  // with the lazy move of the running max.
+  __device__ __forceinline__ void softmax_phase(int t) {
+    if (t < 0 || t >= ntw) return;
+    const int k0 = t * BC;
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
+    if (need_mask) {
+      // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset)
+      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 8 * g;
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-      mx = fmaxf(mx, swap_halves(mx)) * sl2;
-      // Move the running max only when some query's probabilities would grow
-      // past 2^threshold (always on the first visible tile, where m = -inf).
-      if (__ballot(mx > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mx);
-        // a query with every key so far masked keeps m = -inf and nothing to rescale
-        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(fmaf(s[sb][i], sl2, -m_use));
-          s[sb][i] = p;
-          rs += p;
-        }
-      l_part += rs;
-      // O^T += V^T P^T over the tile's four 16-key chunks.  B operand: P^T
-      // chunk kc2 (keys k0 + 16 kc2 + 8 g + 0..7 of this lane's query).  A
-      // operand: V^T rows 32 db + c32, read transposed from the V tile.
-#pragma unroll
-      for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
-        float t[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) t[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
-        const bf16x8 pb = pack8(t);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 va = join_tr(lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 0)),
-                                    lds_read_tr(Vs + tr.off(16 * kc2, 32 * db, 1)));
-          oacc[db] = mfma32(va, pb, oacc[db]);
-        }
-      }
+        for (int i = 0; i < 16; ++i)
+          if (32 * sb + 16 * (i >> 3) + (i & 7) > lim) s[sb][i] = -INFINITY;
     }
-    wait_vmem();
-    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < BC / 32; ++sb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+    mx = max_halves(mx) * sl2;
+    // Move the running max only when some query's probabilities would grow
+    // past 2^threshold (always on the first visible tile, where m = -inf).
+    if (__ballot(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      // a query with every key so far masked keeps m = -inf and nothing to rescale
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
+      float p[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        p[jj] = exp2_fast(fmaf(s[kc2 >> 1][(kc2 & 1) * 8 + jj], sl2, -m_use));
+        rs += p[jj];
+      }
+      pb[kc2] = pack8(p);
+    }
+    l_part += rs;
+  }
+
+  // One period (two barrier-separated slots) of a wave of group GRP.  R = t
+  // mod 3 names the buffers: K tile t in K buffer R, V tile t - 1 in V buffer
+  // (R + 2) mod 3.  The period also starts the copies of K tile t + 2 (into
+  // the buffer of K tile t - 1) and V tile t + 1 (into the buffer of V tile
+  // t - 2), both last read in the previous period, and ends once K tile t + 1
+  // and V tile t are in LDS for the next one.  Group 0 runs the matrix phase
+  // of tile t in the first slot and its softmax phase in the second; group 1
+  // runs the softmax phase of tile t - 1 and then the matrix phase of tile t.
+  template <int R, int GRP>
+  __device__ __forceinline__ void period(int t) {
+    constexpr int KB = R, VB = (R + 2) % 3, KN = (R + 2) % 3, VN = (R + 1) % 3;
+    const bool kn = t + 2 < nt, vn = t + 1 < nt;
+    // each wave starts its share of the copies in its softmax slot, off the
+    // matrix phase's critical path
+    if (GRP == 0) {
+      matrix_phase<KB, VB>(t);
+    } else {
+      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t + 1) * BC, N, w, lane);
+      softmax_phase(t - 1);
+    }
+    block_barrier();
+    if (GRP == 0) {
+      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t + 1) * BC, N, w, lane);
+      softmax_phase(t);
+    } else {
+      matrix_phase<KB, VB>(t);
+    }
+    if (kn) wait_vmem_except_last<2 * C::COPIES>();
+    else if (vn) wait_vmem_except_last<C::COPIES>();
+    else wait_vmem();
+    block_barrier();
+  }
+
+  // Periods 0 .. nt (the last one only finishes O^T += V^T P^T of the last
+  // tile).  Both groups pass the same sequence of barriers.
+  template <int GRP>
+  __device__ __forceinline__ void run() {
+    for (int t = 0; t <= nt; t += 3) {
+      period<0, GRP>(t);
+      if (t + 1 > nt) break;
+      period<1, GRP>(t + 1);
+      if (t + 2 > nt) break;
+      period<2, GRP>(t + 2);
+    }
   }
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int TILE = C::TILE;
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k2s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v2s[TILE];
 
   const int tid = threadIdx.x;
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
 
   // Workgroup -> (head, query block).  Consecutive workgroup ids land on
-  // different XCDs (round robin over 8); give each XCD a contiguous run of
-  // work so the query blocks of one head share that XCD's L2.  Within a head
-  // the heaviest (last) causal blocks go first.
+  // different XCDs (round robin over 8).  When the heads split evenly over
+  // the XCDs, XCD x takes heads x * BH/8 .. and walks them query block by
+  // query block, heaviest causal blocks first, so each head's K and V stay
+  // in one XCD's L2 and the longest blocks start first; otherwise each XCD
+  // takes a contiguous run of (head, block) pairs.
   const int total = gridDim.x;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int bh = L / nqb;
-  int qb = L - bh * nqb;
+  int bh, qb;
+  if ((a.BH & 7) == 0) {
+    const int hpx = a.BH >> 3;  // heads per XCD
+    const int j = blockIdx.x >> 3;
+    bh = (blockIdx.x & 7) * hpx + j % hpx;
+    qb = j / hpx;
+  } else {
+    int L = blockIdx.x;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    bh = L / nqb;
+    qb = L - bh * nqb;
+  }
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;
-  FwdBlock<D, CAUSAL> f;
-  f.sm = FwdSmem<D>{k0s, v0s, k1s, v1s};
+  FwdWave<D, CAUSAL> f;
+  f.sm = FwdSmem{{k0s, k1s, k2s}, {v0s, v1s, v2s}};
   f.Kh = a.k + hoff;
   f.Vh = a.v + hoff;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  // Waves w and w + 4 run on the same SIMD: they form a ping-pong pair and
+  // take adjacent 32-row chunks, so the pair's causal work is balanced.
+  f.grp = f.w >> 2;
   f.lane = tid & 63;
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
   f.N = N;
   const int q0 = qb * C::BR;
-  f.qw0 = q0 + f.w * C::QW;
+  f.qw0 = q0 + (2 * (f.w & 3) + f.grp) * C::QW;
   f.qrow = f.qw0 + f.c32;  // the query this lane owns
   f.nt = (N + C::BC - 1) / C::BC;
   if (CAUSAL) f.nt = min(f.nt, (q0 + C::BR + C::BC - 1) / C::BC);
+  f.ntw = CAUSAL ? min(f.nt, (f.qw0 + C::QW + C::BC - 1) / C::BC) : f.nt;
   f.sl2 = a.scale_log2;
   f.m_run = -INFINITY;
   f.l_part = 0.f;
@@ -288,7 +354,10 @@ fa_fwd_kernel(FwdArgs a) {
   f.ku = f.g ^ chunk_swizzle<D>(f.c32);
   f.cp.init(f.w, f.lane);
 
-  f.template issue<0>(0);
+  // K tiles 0 and 1 and V tile 0 before the first period.
+  f.cp.template issue<true>(f.Kh, k0s, 0, N, f.w, f.lane);
+  if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, C::BC, N, f.w, f.lane);
+  f.cp.template issue<false>(f.Vh, v0s, 0, N, f.w, f.lane);
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
   const uint16_t* Qh = a.q + hoff;
 #pragma unroll
@@ -298,17 +367,13 @@ fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) f.oacc[db] = zero16();
   wait_vmem();
-  __syncthreads();
+  block_barrier();
 
-  int j = 0;
-  for (; j + 1 < f.nt; j += 2) {
-    f.template step<0>(j);
-    f.template step<1>(j + 1);
-  }
-  if (j < f.nt) f.template step<0>(j);
+  if (f.grp == 0) f.template run<0>();
+  else f.template run<1>();
 
   // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
-  const float l = f.l_part + swap_halves(f.l_part);
+  const float l = sum_halves(f.l_part);
   if (f.qrow < N) {
     const float inv = 1.f / l;
     uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
