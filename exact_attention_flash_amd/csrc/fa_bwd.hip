@@ -316,15 +316,11 @@ fa_bwd_kv_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkb = (N + C::BCK - 1) / C::BCK;
-  // Workgroup -> (head, key block), XCD-contiguous (consecutive ids land on
-  // different XCDs, round robin over 8) so the key blocks of one head share
-  // that XCD's L2.  Causal key blocks near the start see the most query
-  // blocks, so the natural order is already heaviest first.
-  const int total = gridDim.x;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int bh = L / nkb;
-  const int kb = L - bh * nkb;
+  // Workgroup -> (head, key block): heads grouped per XCD; causal key blocks
+  // near the start see the most query blocks, so run order is already
+  // heaviest first.
+  int bh, kb;
+  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nkb, bh, kb);
 
   KvBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
   const int nqb = blk.nqb;
@@ -488,13 +484,10 @@ fa_bwd_q_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
-  // Workgroup -> (head, query block): XCD-contiguous, heaviest causal
-  // blocks first within a head (as in the forward pass).
-  const int total = gridDim.x;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int bh = L / nqb;
-  int qb = L - bh * nqb;
+  // Workgroup -> (head, query block): heads grouped per XCD, heaviest
+  // (last) causal query blocks first.
+  int bh, qb;
+  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;

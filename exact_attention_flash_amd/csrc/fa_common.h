@@ -80,6 +80,29 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup id -> (head, block-in-run-order) for a grid of BH * nblk
+// workgroups.  Consecutive workgroup ids land on different XCDs (round robin
+// over 8).  When the heads split evenly over the XCDs, XCD x takes heads
+// x * BH/8 .. x * BH/8 + BH/8 - 1 and walks them block by block (run order 0
+// for every head first, then 1, ...), so a head's K and V stay in one XCD's
+// L2 and callers that map run order 0 to their heaviest block start the
+// longest work first.  Otherwise each XCD takes a contiguous run of
+// (head, block) pairs.
+__device__ __forceinline__ void xcd_head_block(int wg, int total, int BH, int nblk, int& bh,
+                                               int& blk) {
+  if ((BH & 7) == 0) {
+    const int hpx = BH >> 3;
+    const int j = wg >> 3;
+    bh = (wg & 7) * hpx + j % hpx;
+    blk = j / hpx;
+  } else {
+    int L = wg;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    bh = L / nblk;
+    blk = L - bh * nblk;
+  }
+}
+
 // Workgroup barrier without a memory fence: unlike __syncthreads() it does
 // not wait for this wave's outstanding global -> LDS copies.  The compiler
 // may not move memory operations across it.  Callers wait for the copies a

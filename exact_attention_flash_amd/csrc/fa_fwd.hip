@@ -306,25 +306,10 @@ fa_fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
 
-  // Workgroup -> (head, query block).  Consecutive workgroup ids land on
-  // different XCDs (round robin over 8).  When the heads split evenly over
-  // the XCDs, XCD x takes heads x * BH/8 .. and walks them query block by
-  // query block, heaviest causal blocks first, so each head's K and V stay
-  // in one XCD's L2 and the longest blocks start first; otherwise each XCD
-  // takes a contiguous run of (head, block) pairs.
-  const int total = gridDim.x;
+  // Workgroup -> (head, query block): heads grouped per XCD, heaviest
+  // (last) causal query blocks first.
   int bh, qb;
-  if ((a.BH & 7) == 0) {
-    const int hpx = a.BH >> 3;  // heads per XCD
-    const int j = blockIdx.x >> 3;
-    bh = (blockIdx.x & 7) * hpx + j % hpx;
-    qb = j / hpx;
-  } else {
-    int L = blockIdx.x;
-    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-    bh = L / nqb;
-    qb = L - bh * nqb;
-  }
+  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;
