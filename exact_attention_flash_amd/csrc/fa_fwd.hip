@@ -106,7 +106,8 @@ struct TileCopy {
     } else {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t) {
-        const int r = KEYS ? swap23(slot_row(t, w, lane)) : slot_row(t, w, lane);
+        // not worth a register across the loop
+        const int r = opaque(KEYS ? swap23(slot_row(t, w, lane)) : slot_row(t, w, lane));
         const int shift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
         buffer_load_lds16_unseen(rs, (KEYS ? koff[t] : voff[t]) + shift,
                                  Ts + (t * C::NW + w) * 64 * 8);
@@ -200,7 +201,7 @@ struct FwdWave {
     const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
     if (need_mask) {
       // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset)
-      const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 8 * g;
+      const int lim = opaque((CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 8 * g);
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
