@@ -320,7 +320,7 @@ fa_bwd_kv_kernel(BwdArgs a) {
   // near the start see the most query blocks, so run order is already
   // heaviest first.
   int bh, kb;
-  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nkb, bh, kb);
+  xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nkb, bh, kb);
 
   KvBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
   const int nqb = blk.nqb;
@@ -487,7 +487,7 @@ fa_bwd_q_kernel(BwdArgs a) {
   // Workgroup -> (head, query block): heads grouped per XCD, heaviest
   // (last) causal query blocks first.
   int bh, qb;
-  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
+  xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;

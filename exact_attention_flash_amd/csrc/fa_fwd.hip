@@ -310,7 +310,7 @@ fa_fwd_kernel(FwdArgs a) {
   // Workgroup -> (head, query block): heads grouped per XCD, heaviest
   // (last) causal query blocks first.
   int bh, qb;
-  xcd_head_block(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
+  xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;

@@ -47,6 +47,10 @@ SMALL_FWD = [
     (2, 2, 333, 128, False),
     (1, 3, 513, 64, False),
     (1, 1, 256, 128, True),
+    # B*H a multiple of 8 (heads grouped per XCD), several 256-row query
+    # blocks with a ragged last one
+    (2, 4, 600, 128, True),
+    (1, 8, 520, 64, False),
 ]
 
 
@@ -101,6 +105,9 @@ SMALL_BWD = [
     (1, 1, 1, 64, True),
     (1, 2, 77, 128, False),
     (1, 1, 300, 64, False),
+    # B*H a multiple of 8 (heads grouped per XCD), ragged blocks
+    (2, 4, 333, 128, True),
+    (1, 8, 270, 64, False),
 ]
 
 
