@@ -59,6 +59,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.flash_attn_bwd_q_blocks.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                 i64, i64, i64, i64, ci, fl, vp]
         lib.flash_attn_bwd_q_blocks.restype = ci
+        lib.flash_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                               i64, i64, i64, i64, ci, fl, i64, vp]
+        lib.flash_attn_fwd_splitkv.restype = ci
+        lib.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        lib.flash_attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -126,6 +131,44 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
         st = lib.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), B, H, N, d, int(bool(causal)), scale,
                                 _stream_ptr(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_fwd_splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+    return int(load_library().flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
+
+
+def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           num_splits: int, causal: bool = False,
+                           softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                           lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None):
+    """``flash_attn_fwd`` with each query block's keys cut into ``num_splits``
+    ranges and merged; returns ``(out, lse)``."""
+    B, H, N, d = _check_tensors(q, k, v, names="q,k,v")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out, names="q,out")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    lib = load_library()
+    need = int(lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        B, H, N, d, int(bool(causal)), scale, int(num_splits),
+                                        _stream_ptr(q.device, stream))
     _check(st)
     return out, lse
 

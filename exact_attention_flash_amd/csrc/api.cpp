@@ -15,6 +15,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // keeps every byte count in int64
 constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxSplits = 128;              // split-KV ranges per query block
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -75,6 +76,13 @@ size_t ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   (void)d;
   const size_t prow = size_t(B) * size_t(H) * size_t(padded_rows(N));
   return 2 * round_up(prow * 4, kWsAlign);
+}
+
+// Split-KV workspace: fp32 partial O [S, B*H, N, d], then the fp32 running
+// max and row sum [S, B*H, N] each, every section 256-byte aligned.
+size_t splitkv_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t S) {
+  const size_t rows = size_t(S) * size_t(B) * size_t(H) * size_t(N);
+  return round_up(rows * size_t(d) * 4, kWsAlign) + 2 * round_up(rows * 4, kWsAlign);
 }
 
 // Pointers of the backward pass; `used` selects the ones a stage reads or
@@ -237,6 +245,58 @@ int flash_attn_bwd_q_blocks(const void* q, const void* k, const void* v, const v
                  hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+                                              int64_t num_splits) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, &empty) != FA_OK || empty) return 0;
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return splitkv_ws_bytes(B, H, N, d, num_splits);
+}
+
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float softmax_scale,
+                           int64_t num_splits, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_BAD_SPLITS;
+  if (empty) return FA_OK;
+  // the partial kernel's grid: 256-row query blocks x heads x ranges
+  if (((N + 255) / 256) * (B * H) * num_splits > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA_ERR_MISALIGNED;
+  const size_t need = splitkv_ws_bytes(B, H, N, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tb = size_t(B * H * N * d) * 2, lb = size_t(B * H * N) * 4;
+  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range outs[3] = {range_of(o, tb), range_of(lse, lb), range_of(workspace, need)};
+  if (any_alias(outs, 3, ins, 3)) return FA_ERR_ALIASING;
+
+  const size_t rows = size_t(num_splits) * size_t(B * H) * size_t(N);
+  char* ws = static_cast<char*>(workspace);
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = int(N);
+  a.BH = int(B * H);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.splits = int(num_splits);
+  a.opart = reinterpret_cast<float*>(ws);
+  a.mpart = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign));
+  a.lpart = reinterpret_cast<float*>(ws + round_up(rows * size_t(d) * 4, kWsAlign) +
+                                     round_up(rows * 4, kWsAlign));
+  const hipError_t e =
+      fa::launch_fwd_splitkv(a, int(d), causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -248,6 +308,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than flash_attn_bwd_workspace_bytes()";
     case FA_ERR_ALIASING: return "an output buffer overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 128";
     default: return "unknown status";
   }
 }

@@ -132,7 +132,9 @@ struct FwdWave {
   FwdSmem sm;
   const uint16_t* Kh;
   const uint16_t* Vh;
-  int w, grp, lane, c32, g, N, qw0, qrow, nt, ntw;
+  int w, grp, lane, c32, g, N, qw0, qrow;
+  int t0;       // first key tile of this workgroup's key range
+  int nt, ntw;  // tiles in the range; of those, tiles this wave sees (causal)
   float sl2;
   float m_run;   // running max of scale*log2(e)*s (possibly stale)
   float l_part;  // this lane's share of the running row sum
@@ -197,7 +199,7 @@ struct FwdWave {
   // with the lazy move of the running max.
   __device__ __forceinline__ void softmax_phase(int t) {
     if (t < 0 || t >= ntw) return;
-    const int k0 = t * BC;
+    const int k0 = (t0 + t) * BC;
     const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
     if (need_mask) {
       // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset)
@@ -259,14 +261,14 @@ struct FwdWave {
     if (GRP == 0) {
       matrix_phase<KB, VB>(t);
     } else {
-      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
       softmax_phase(t - 1);
     }
     block_barrier();
     if (GRP == 0) {
-      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
       softmax_phase(t);
     } else {
       matrix_phase<KB, VB>(t);
@@ -291,7 +293,9 @@ struct FwdWave {
   }
 };
 
-template <int D, bool CAUSAL>
+// SPLIT: workgroup = (head, query block, key range); writes the range's
+// unnormalised partials (see FwdArgs) instead of O and LSE.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
@@ -307,10 +311,13 @@ fa_fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
 
-  // Workgroup -> (head, query block): heads grouped per XCD, heaviest
-  // (last) causal query blocks first.
+  // Workgroup -> (head, query block[, key range]): heads grouped per XCD,
+  // heaviest (last) causal query blocks first.
+  const int split = SPLIT ? (int)(blockIdx.x % (unsigned)a.splits) : 0;
+  const int wg = SPLIT ? (int)(blockIdx.x / (unsigned)a.splits) : (int)blockIdx.x;
+  const int total = SPLIT ? (int)(gridDim.x / (unsigned)a.splits) : (int)gridDim.x;
   int bh, qb;
-  xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nqb, bh, qb);
+  xcd_head_block<kHeadsPerGroup>(wg, total, a.BH, nqb, bh, qb);
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;
@@ -329,9 +336,14 @@ fa_fwd_kernel(FwdArgs a) {
   const int q0 = qb * C::BR;
   f.qw0 = q0 + (2 * (f.w & 3) + f.grp) * C::QW;
   f.qrow = f.qw0 + f.c32;  // the query this lane owns
-  f.nt = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) f.nt = min(f.nt, (q0 + C::BR + C::BC - 1) / C::BC);
-  f.ntw = CAUSAL ? min(f.nt, (f.qw0 + C::QW + C::BC - 1) / C::BC) : f.nt;
+  // key tiles the block sees, then this workgroup's range of them
+  int nt_all = (N + C::BC - 1) / C::BC;
+  if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + C::BC - 1) / C::BC);
+  f.t0 = SPLIT ? split * nt_all / a.splits : 0;
+  const int t1 = SPLIT ? (split + 1) * nt_all / a.splits : nt_all;
+  f.nt = t1 - f.t0;
+  const int ntw_all = CAUSAL ? min(nt_all, (f.qw0 + C::QW + C::BC - 1) / C::BC) : nt_all;
+  f.ntw = max(0, min(f.nt, ntw_all - f.t0));
   f.sl2 = a.scale_log2;
   f.m_run = -INFINITY;
   f.l_part = 0.f;
@@ -340,10 +352,13 @@ fa_fwd_kernel(FwdArgs a) {
   f.ku = f.g ^ chunk_swizzle<D>(f.c32);
   f.cp.init(f.w, f.lane);
 
-  // K tiles 0 and 1 and V tile 0 before the first period.
-  f.cp.template issue<true>(f.Kh, k0s, 0, N, f.w, f.lane);
-  if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, C::BC, N, f.w, f.lane);
-  f.cp.template issue<false>(f.Vh, v0s, 0, N, f.w, f.lane);
+  // K tiles 0 and 1 and V tile 0 of the range before the first period (an
+  // empty range, possible only for a split, skips the loop altogether).
+  if (f.nt > 0) {
+    f.cp.template issue<true>(f.Kh, k0s, f.t0 * C::BC, N, f.w, f.lane);
+    if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, (f.t0 + 1) * C::BC, N, f.w, f.lane);
+    f.cp.template issue<false>(f.Vh, v0s, f.t0 * C::BC, N, f.w, f.lane);
+  }
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
   const uint16_t* Qh = a.q + hoff;
 #pragma unroll
@@ -355,11 +370,34 @@ fa_fwd_kernel(FwdArgs a) {
   wait_vmem();
   block_barrier();
 
-  if (f.grp == 0) f.template run<0>();
-  else f.template run<1>();
+  if (f.nt > 0) {
+    if (f.grp == 0) f.template run<0>();
+    else f.template run<1>();
+  }
 
-  // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
   const float l = sum_halves(f.l_part);
+  if (SPLIT) {
+    // the range's partials, relative to its own running max
+    if (f.qrow < N) {
+      const int64_t row = ((int64_t)split * a.BH + bh) * N + f.qrow;
+      float* Orow = a.opart + row * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = f.oacc[db][4 * r4 + e];
+          *reinterpret_cast<f32x4*>(Orow + db * 32 + 8 * r4 + 4 * f.g) = val;
+        }
+      if (f.g == 0) {
+        a.mpart[row] = f.m_run;
+        a.lpart[row] = l;
+      }
+    }
+    return;
+  }
+  // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
   if (f.qrow < N) {
     const float inv = 1.f / l;
     uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
@@ -376,18 +414,78 @@ fa_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Merge of the split-KV partials (Flash-Decoding's combine step, CMU notes
+// section "Flash-Decoding"; the two-block merge of section "安全 Softmax 与
+// 在线 Softmax" applied over all ranges at once): per row
+//   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
+//   O = sum_s w_s O_s / L,  LSE = (M + log2 L) ln 2.
+// A range that saw no visible key has m_s = -inf, l_s = 0, O_s = 0 and
+// weight 0.  D / 4 threads per row, 4 columns each.
+template <int D>
+__global__ void __launch_bounds__(256) fa_fwd_merge_kernel(FwdArgs a) {
+  constexpr int TPR = D / 4;        // threads per row
+  constexpr int RPB = 256 / TPR;    // rows per workgroup
+  const int64_t rows = (int64_t)a.BH * a.N;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int col = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;
+  const int64_t plane = rows;       // rows per split
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.mpart[s * plane + row]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.splits; ++s) {
+    const float m = a.mpart[s * plane + row];
+    const float wgt = m == -INFINITY ? 0.f : exp2_fast(m - M);
+    L = fmaf(wgt, a.lpart[s * plane + row], L);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(a.opart + (s * plane + row) * D + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, o[e], acc[e]);
+  }
+  const float inv = 1.f / L;
+  u32x2 val;
+  val.x = pack2(acc[0] * inv, acc[1] * inv);
+  val.y = pack2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(a.o + row * D + col) = val;
+  if (col == 0) a.lse[row] = (M + log2_fast(L)) * kLn2;
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int64_t nqb = (a.N + C::BR - 1) / C::BR;
   const int64_t grid = nqb * a.BH;
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_splitkv_t(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int64_t nqb = (a.N + C::BR - 1) / C::BR;
+  const int64_t grid = nqb * a.BH * a.splits;
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t rows = (int64_t)a.BH * a.N;
+  hipLaunchKernelGGL((fa_fwd_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 64) return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
   return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+}
+
+hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_fwd_splitkv_t<64, true>(a, stream) : launch_fwd_splitkv_t<64, false>(a, stream);
+  return causal ? launch_fwd_splitkv_t<128, true>(a, stream)
+                : launch_fwd_splitkv_t<128, false>(a, stream);
 }
 
 }  // namespace fa

@@ -17,6 +17,17 @@ struct FwdArgs {
   int N;              // sequence length
   int BH;             // B * H
   float scale_log2;   // softmax_scale * log2(e), > 0
+  // Split-KV forward only (splits > 1 or partials requested): each query
+  // block's key tiles are cut into `splits` contiguous ranges, one
+  // workgroup per range, whose unnormalised partial results go to
+  //   opart  fp32 [splits, B*H, N, d]  (sum of 2^(s - m) V over the range)
+  //   mpart  fp32 [splits, B*H, N]     running max m, log2 units, scaled
+  //   lpart  fp32 [splits, B*H, N]     sum of 2^(s - m) over the range
+  // and a merge kernel writes O and LSE.
+  int splits = 1;
+  float* opart = nullptr;
+  float* mpart = nullptr;
+  float* lpart = nullptr;
 };
 
 // Query rows per block of the backward key-block pass; the row vectors in
@@ -44,6 +55,10 @@ struct BwdArgs {
 
 // Enqueue the forward kernel for head dim d (64 or 128).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Enqueue the split-KV forward: the partial kernel over a.splits key ranges
+// per query block, then the merge kernel that writes O and LSE.
+hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // The three backward stages, each one kernel launch, for head dim d (64 or
 // 128): the row pass, the pass over key blocks (dK, dV) and the pass over

@@ -67,7 +67,8 @@ enum fa_status {
   FA_ERR_BAD_SCALE = 5,           /* softmax_scale is NaN, Inf or <= 0 */
   FA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the required size */
   FA_ERR_ALIASING = 7,            /* an output overlaps an input or output */
-  FA_ERR_HIP = 8                  /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 8,                 /* the HIP runtime rejected a launch */
+  FA_ERR_BAD_SPLITS = 9           /* num_splits outside 1..128 (split-KV forward) */
 };
 
 /*
@@ -86,6 +87,45 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
                    void* o, float* lse,
                    int64_t B, int64_t H, int64_t N, int64_t d,
                    int causal, float softmax_scale, void* stream);
+
+/*
+ * Split-KV forward: the same O and LSE as flash_attn_fwd, computed with the
+ * key tiles of every query block cut into num_splits contiguous ranges, one
+ * workgroup per (head, query block, range), followed by a merge kernel.
+ * This is the combine step of Flash-Decoding (CMU notes, section
+ * "Flash-Decoding": the per-block statistics (m, l) merge associatively and
+ * commutatively, section "安全 Softmax 与在线 Softmax"): each range yields
+ * an unnormalised partial output with its own running max m_s and row sum
+ * l_s, and per row
+ *   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,
+ *   O = sum_s 2^(m_s - M) O_s / L,  LSE = (M + log2 L) ln 2
+ * (m in log2 units of the scaled scores).  It fills the GPU when
+ * B * H * ceil(N / 256) is small.  Results agree with flash_attn_fwd to
+ * rounding (not bitwise: the sums are grouped differently).
+ *   q, k, v, o, lse, causal, softmax_scale : as flash_attn_fwd
+ *   workspace  : device memory of at least
+ *                flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits)
+ *                bytes, 16-byte aligned, caller-owned, no initialisation;
+ *                it must not overlap any other argument
+ *   num_splits : 1 .. 128 key ranges per query block (ranges with no key a
+ *                query sees contribute nothing); FA_ERR_BAD_SPLITS otherwise
+ * Two launches on `stream`.  Deterministic.
+ */
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           int causal, float softmax_scale, int64_t num_splits,
+                           void* stream);
+
+/*
+ * Bytes of workspace flash_attn_fwd_splitkv needs: fp32 partial outputs
+ * [num_splits, B*H, N, d], then the fp32 running max and row sum
+ * [num_splits, B*H, N] each, every section rounded up to 256 bytes.  Returns
+ * 0 for an empty problem and for invalid sizes or num_splits.
+ */
+size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+                                              int64_t num_splits);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape: two fp32

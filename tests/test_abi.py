@@ -19,7 +19,7 @@ from exact_attention_flash_amd.binding import LIB_PATH, load_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR = range(9)
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS = range(10)
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                             reason="fake-pointer validation runs only without a GPU")
@@ -36,7 +36,8 @@ def test_library_exports_header_symbols():
     assert names == sorted(["flash_attn_fwd", "flash_attn_bwd",
                             "flash_attn_bwd_workspace_bytes", "flash_attn_status_string",
                             "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
-                            "flash_attn_bwd_q_blocks"])
+                            "flash_attn_bwd_q_blocks", "flash_attn_fwd_splitkv",
+                            "flash_attn_fwd_splitkv_workspace_bytes"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -47,7 +48,7 @@ def test_library_exports_header_symbols():
 
 def test_status_strings():
     lib = load_library()
-    for s in range(9):
+    for s in range(10):
         assert lib.flash_attn_status_string(s) not in (None, b"unknown status")
     assert lib.flash_attn_status_string(99) == b"unknown status"
 
@@ -62,6 +63,18 @@ def test_workspace_bytes():
     assert lib.flash_attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert lib.flash_attn_bwd_workspace_bytes(1, 1, 10, 96) == 0
     assert lib.flash_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
+
+
+def test_splitkv_workspace_bytes():
+    lib = load_library()
+    rows = 4 * 2 * 8 * 1024
+    # fp32 partial O [S, B*H, N, d], then fp32 m and l [S, B*H, N]
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(2, 8, 1024, 64, 4) == rows * 64 * 4 + 2 * rows * 4
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 3, 128, 1) == 3 * 128 * 4 + 2 * 256
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 16, 64, 0) == 0
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 16, 64, 129) == 0
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(0, 1, 16, 64, 2) == 0
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 16, 96, 2) == 0
 
 
 A = 1 << 20  # fake, 16-byte-aligned addresses spaced far apart
@@ -89,6 +102,32 @@ def test_fwd_validation():
     assert _fwd(lib, o=A) == ALIAS                       # O on top of Q
     assert _fwd(lib, lse=4 * A + 16) == ALIAS            # LSE inside O
     assert _fwd(lib, o=A + 16 * 64 * 2) != ALIAS         # O just after Q
+
+
+def _fwd_split(lib, ws_bytes=None, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, ws=6 * A, B=1, H=1,
+               N=16, d=64, causal=0, scale=0.125, splits=2):
+    need = lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits)
+    wsb = need if ws_bytes is None else ws_bytes
+    return lib.flash_attn_fwd_splitkv(q, k, v, o, lse, ws, wsb, B, H, N, d, causal, scale, splits,
+                                      None)
+
+
+@no_gpu
+def test_fwd_splitkv_validation():
+    lib = load_library()
+    assert _fwd_split(lib, B=0, ws=None) == FA_OK            # empty: no-op
+    assert _fwd_split(lib, splits=0) == SPLITS
+    assert _fwd_split(lib, splits=129) == SPLITS
+    assert _fwd_split(lib, B=0, splits=0) == SPLITS          # checked even when empty
+    assert _fwd_split(lib, ws=None) == NULLP
+    assert _fwd_split(lib, q=None) == NULLP
+    assert _fwd_split(lib, ws=6 * A + 8) == MISAL
+    assert _fwd_split(lib, d=96) == HEADDIM
+    assert _fwd_split(lib, scale=float("nan")) == SCALE
+    assert _fwd_split(lib, ws_bytes=1024) == WS
+    assert _fwd_split(lib, ws=A) == ALIAS                    # workspace on top of Q
+    assert _fwd_split(lib, ws=4 * A) == ALIAS                # workspace on top of O
+    assert _fwd_split(lib, o=3 * A) == ALIAS                 # O on top of V
 
 
 def _bwd(lib, ws_bytes=None, **kw):
@@ -150,6 +189,7 @@ def test_valid_call_without_device_reports_hip_error():
     because nothing can run)."""
     lib = load_library()
     assert _fwd(lib) == HIPERR
+    assert _fwd_split(lib) == HIPERR
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_flash_amd import flash_attn_bwd, flash_attn_fwd
+from exact_attention_flash_amd import flash_attn_bwd, flash_attn_fwd, flash_attn_fwd_splitkv
 from exact_attention_flash_amd.inputs import WORKLOADS, default_scale, make_inputs
 
 from gpu_util import (bf16_to_f64, check_grad, check_lse, check_o, to_device)
@@ -31,6 +31,13 @@ def _say(msg):
 def _run_fwd(x, causal, scale):
     q, k, v = (to_device(x[n]) for n in ("q", "k", "v"))
     o, lse = flash_attn_fwd(q, k, v, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return (q, k, v), o, lse
+
+
+def _run_fwd_split(x, causal, scale, splits):
+    q, k, v = (to_device(x[n]) for n in ("q", "k", "v"))
+    o, lse = flash_attn_fwd_splitkv(q, k, v, splits, causal=causal, softmax_scale=scale)
     torch.cuda.synchronize()
     return (q, k, v), o, lse
 
@@ -63,6 +70,38 @@ def test_fwd_small_full_parity(B, H, N, d, causal):
     O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
     check_o(bf16_to_f64(o), O_ref)
     check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
+
+
+SPLIT_FWD = [
+    # (B, H, N, d, causal, num_splits)
+    (1, 1, 128, 64, False, 2),
+    (1, 2, 200, 64, True, 3),
+    (2, 1, 333, 128, False, 4),
+    (1, 1, 1000, 128, True, 7),
+    (1, 1, 63, 64, True, 5),      # one key tile: four empty ranges
+    (1, 1, 1, 128, False, 3),
+    (2, 4, 600, 128, True, 16),   # more ranges than some blocks' tiles
+    (1, 3, 513, 64, False, 1),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,splits", SPLIT_FWD)
+def test_fwd_splitkv_small_full_parity(B, H, N, d, causal, splits):
+    _say(f"fwd split-KV B={B} H={H} N={N} d={d} causal={causal} splits={splits}")
+    x = make_inputs(B, H, N, d, seed=N * 5 + d + causal + splits)
+    scale = default_scale(d)
+    _, o, lse = _run_fwd_split(x, causal, scale, splits)
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    check_o(bf16_to_f64(o), O_ref)
+    check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
+
+
+def test_fwd_splitkv_deterministic():
+    x = make_inputs(1, 2, 700, 128, seed=5)
+    scale = default_scale(128)
+    _, o1, l1 = _run_fwd_split(x, True, scale, 5)
+    _, o2, l2 = _run_fwd_split(x, True, scale, 5)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -133,11 +172,15 @@ def _sample_rows(N, rng, n=96):
     return np.unique(np.array(edge + mid, dtype=np.int64))
 
 
-def _fwd_workload(name, causal, q_mult, full_heads_max):
+def _fwd_workload(name, causal, q_mult, full_heads_max, splits=None):
     wl = WORKLOADS[name]
-    _say(f"workload {name} causal={causal} q_mult={q_mult} shape=({wl.B},{wl.H},{wl.N},{wl.d})")
+    _say(f"workload {name} causal={causal} q_mult={q_mult} splits={splits} "
+         f"shape=({wl.B},{wl.H},{wl.N},{wl.d})")
     x = make_inputs(wl.B, wl.H, wl.N, wl.d, seed=wl.seed, q_mult=q_mult)
-    _, o, lse = _run_fwd(x, causal, wl.scale)
+    if splits is None:
+        _, o, lse = _run_fwd(x, causal, wl.scale)
+    else:
+        _, o, lse = _run_fwd_split(x, causal, wl.scale, splits)
     o64 = bf16_to_f64(o)
     l64 = lse.cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(wl.seed)
@@ -170,6 +213,14 @@ def test_workload_c1():
 
 def test_workload_c2():
     _fwd_workload("c2", True, 1.0, 16)
+
+
+def test_workload_c1_splitkv():
+    _fwd_workload("c1", False, 1.0, 1, splits=2)
+
+
+def test_workload_c2_splitkv():
+    _fwd_workload("c2", True, 1.0, 16, splits=4)
 
 
 @pytest.mark.parametrize("causal", [False, True])
