@@ -45,6 +45,10 @@ def parse_args():
     ap.add_argument("--workload", default="c5", help="named workload (default c5: fwd+bwd)")
     ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the step the CPU oracle times (0 = skip cpu_baseline)")
+    ap.add_argument("--splitkv", type=int, default=0,
+                    help="also time the forward on small-grid shapes (c2's, and few heads with "
+                         "long sequences) plain and split-KV with this many key ranges "
+                         "(0 = skip); reported under 'splitkv'")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters); not timed")
@@ -102,6 +106,51 @@ def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
                    f"N={wl.N}, d={wl.d}, causal), float64 numpy, {dt:.2f} s; "
                    f"same flop convention as value"),
     }
+
+
+# Split-KV comparison shapes (B, H, N, d, causal, seed): c2's shape (64
+# workgroups for 256 CUs) and few heads with long sequences.
+SPLITKV_SHAPES = [(2, 8, 1024, 64, True, 2000), (1, 2, 16384, 128, True, 7001),
+                  (1, 4, 8192, 128, False, 7002)]
+
+
+def splitkv_measure(fa, make_inputs, splits: int, iters: int = 20) -> list:
+    """Forward on small-grid shapes, plain and split-KV, timed with HIP
+    events on the current stream (average over `iters` launches each)."""
+    import numpy as np
+    import torch
+    out = []
+    stream = torch.cuda.current_stream()
+
+    def avg(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for B, H, N, d, causal, seed in SPLITKV_SHAPES:
+        x = make_inputs(B, H, N, d, seed=seed)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(
+            torch.bfloat16).cuda() for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        ws = torch.empty(fa.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits),
+                         dtype=torch.uint8, device=q.device)
+        plain = avg(lambda: fa.flash_attn_fwd(q, k, v, causal=causal, out=o, lse=lse))
+        split = avg(lambda: fa.flash_attn_fwd_splitkv(q, k, v, splits, causal=causal, out=o,
+                                                      lse=lse, workspace=ws))
+        f = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        out.append({"shape": f"{'causal' if causal else 'full'} fwd B={B} H={H} N={N} d={d}",
+                    "num_splits": splits, "plain_ms": round(plain, 4),
+                    "split_ms": round(split, 4), "plain_tflops": round(f / plain / 1e9, 2),
+                    "split_tflops": round(f / split / 1e9, 2)})
+    return out
 
 
 def main() -> int:
@@ -237,6 +286,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.splitkv > 0:
+        line["splitkv"] = splitkv_measure(fa, make_inputs, args.splitkv)
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(x, wl, causal, args.cpu_heads)
     print(json.dumps(line), flush=True)
