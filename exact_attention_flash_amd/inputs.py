@@ -14,6 +14,10 @@ head_dim]``):
 * optional Q multiplier (the large-logit stability case uses 8, a power of
   two, so scaling before or after rounding gives the same bits);
 * float32 -> bf16 with round-to-nearest-even, once.
+
+FP8 variant (``make_inputs_fp8``): the same float32 draws, each tensor
+divided by its own amax / 448 and rounded once to OCP E4M3 (nearest-even,
+saturating); the descale amax / 448 travels with the codes.
 """
 
 from __future__ import annotations
@@ -60,6 +64,69 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, *,
         out[name] = f32_to_bf16_bits(x)
     if with_dout:
         out["do"] = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    return out
+
+
+# ---------------------------------------------------------------- fp8 inputs
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value, 1.75 * 2^8
+
+
+def f32_to_e4m3_bits(x) -> np.ndarray:
+    """Round values to OCP FP8 E4M3 ("E4M3FN"), nearest-even; returns uint8 codes.
+
+    Saturating: magnitudes above 448 give 448.  Finite inputs only.  Layout
+    of a code: sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+    field 0 holds the subnormals m * 2^-9.
+    """
+    a = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(a).astype(np.uint8) << np.uint8(7)
+    mag = np.minimum(np.abs(a), E4M3_MAX)
+    frac, ex = np.frexp(mag)                 # mag = frac * 2^ex, frac in [0.5, 1)
+    e = ex.astype(np.int64) - 1              # mag = (2 frac) * 2^e
+    normal = mag >= 2.0 ** -6  # (zero has e = -1 from frexp, so test the value)
+    # normal range: 3 fraction bits of 2 frac in [1, 2); a carry out of the
+    # fraction moves to the next exponent (never past 448, which is a code)
+    q = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    code_n = ((e + 7) << 3) | q
+    # subnormal range: multiples of 2^-9; 8 * 2^-9 is the smallest normal,
+    # whose code is 8 as well
+    code_s = np.rint(mag * 512.0).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_descale(x) -> float:
+    """Per-tensor dequantisation factor amax / 448, as a float32 value.
+
+    The tensor is stored as codes of x / descale, which puts its largest
+    magnitude at the top of the E4M3 range (amax scaling).  An all-zero
+    tensor gets descale 1.
+    """
+    amax = float(np.max(np.abs(np.asarray(x, dtype=np.float32)))) if np.size(x) else 0.0
+    return float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+
+
+def make_inputs_fp8(B: int, H: int, N: int, d: int, seed: int, *,
+                    q_mult: float = 1.0) -> dict:
+    """Q, K, V as uint8 E4M3 codes of shape [B, H, N, d] with their descales.
+
+    The same float32 draws as ``make_inputs`` (same generator, order and Q
+    multiplier); each tensor then gets its own amax descale and is rounded
+    once to E4M3.  The real value of a code c is descale * e4m3(c).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if name == "q" and q_mult != 1.0:
+            x = x * np.float32(q_mult)
+        ds = e4m3_descale(x)
+        out[name] = f32_to_e4m3_bits(x.astype(np.float64) / ds)
+        out["descale_" + name] = ds
     return out
 
 

@@ -18,6 +18,9 @@ Sources (the web pages this method is described on):
 * "FlashAttention 的基本原理", section 2.4 "反向传播": dV from P^T dO and the
   per-row softmax gradient; the same notes' section
   "为什么前向和反向的并行化策略不同" give dQ_i += dS^(j) K_j.
+* "FlashAttention 系列技术详解", FlashAttention-3 section: FP8 matrix
+  products.  ``fp8`` decodes OCP E4M3 inputs (format from the OCP 8-bit
+  floating point specification) and runs the same exact attention on them.
 
 Every function names the passage it follows.  All arithmetic is float64.
 
@@ -37,6 +40,12 @@ from .attention import (
     attention_forward_rows,
     attention_backward,
 )
+from .fp8 import (
+    decode_e4m3,
+    dequantize,
+    attention_forward_fp8,
+    attention_forward_fp8_rows,
+)
 from .online_softmax import (
     softmax_stats,
     merge_stats,
@@ -53,6 +62,10 @@ __all__ = [
     "attention_forward",
     "attention_forward_rows",
     "attention_backward",
+    "decode_e4m3",
+    "dequantize",
+    "attention_forward_fp8",
+    "attention_forward_fp8_rows",
     "softmax_stats",
     "merge_stats",
     "fold_blocks",

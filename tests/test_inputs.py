@@ -1,6 +1,7 @@
 """Seeded inputs: determinism, bf16 round-to-nearest-even, workload registry."""
 
 import numpy as np
+import pytest
 
 from exact_attention_flash_amd.inputs import (
     WORKLOADS, bf16_bits_to_f32, default_scale, f32_to_bf16_bits, make_inputs,
@@ -58,3 +59,49 @@ def test_workloads_and_flop_convention():
     assert default_scale(64) == 0.125
     assert WORKLOADS["c3"].q_mults == (1.0, 8.0)
     assert WORKLOADS["c4"].N == 16384 and WORKLOADS["c4"].causal == (True,)
+
+
+def _torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_e4m3_encoder_matches_torch():
+    import torch
+    from exact_attention_flash_amd.inputs import f32_to_e4m3_bits
+    # every midpoint between neighbouring finite values (ties to even), both signs
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    fin = np.unique(vals[np.isfinite(vals)])
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    for x in (mids, -mids, fin.astype(np.float32)):
+        assert np.array_equal(f32_to_e4m3_bits(x), _torch_e4m3(x))
+    # random values over many binades, clipped to the finite range
+    r = np.random.default_rng(1)
+    x = np.concatenate([r.standard_normal(20000) * s for s in (1e-3, 0.05, 1, 30, 300)])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    assert np.array_equal(f32_to_e4m3_bits(x), _torch_e4m3(x))
+    # zeros keep their sign; magnitudes past 448 saturate
+    got = f32_to_e4m3_bits(np.array([0.0, -0.0, 500.0, -1e6], dtype=np.float32))
+    assert got.tolist() == [0x00, 0x80, 0x7E, 0xFE]
+
+
+def test_fp8_inputs_share_the_bf16_draws():
+    import torch
+    from exact_attention_flash_amd.inputs import E4M3_MAX, make_inputs_fp8
+    a = make_inputs_fp8(1, 2, 32, 16, seed=9)
+    b = make_inputs_fp8(1, 2, 32, 16, seed=9)
+    f = make_inputs(1, 2, 32, 16, seed=9)
+    for name in ("q", "k", "v"):
+        assert a[name].dtype == np.uint8 and np.array_equal(a[name], b[name])
+        deq = torch.from_numpy(a[name]).view(torch.float8_e4m3fn).double().numpy() \
+            * a["descale_" + name]
+        ref = bf16_bits_to_f32(f[name]).astype(np.float64)
+        # amax scaling: the largest magnitude lands at the top of the range
+        assert np.max(np.abs(deq)) == pytest.approx(np.max(np.abs(ref)), rel=2**-8)
+        assert np.max(np.abs(deq / a["descale_" + name])) <= E4M3_MAX
+        # E4M3 keeps 4 significant bits (normal range): relative error <= 2^-4,
+        # on top of the bf16 rounding of the reference values
+        normal = np.abs(deq / a["descale_" + name]) >= 2**-6
+        rel = np.abs(deq - ref)[normal] / np.abs(ref)[normal]
+        assert rel.max() <= 2**-4 + 2**-7

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import oracle.attention as oa
+import oracle.fp8 as of8
 
 RNG = np.random.default_rng(99)
 B, H, N, d = 1, 1, 6, 3
@@ -99,6 +100,67 @@ def _grad_transposed(p, dp):
     return (p * dp - p * np.sum(p * dp, axis=1, keepdims=True)).T
 
 
+def _e4m3_parts(codes):
+    c = np.asarray(codes).astype(np.int64)
+    return (c >> 7) & 1, (c >> 3) & 0xF, c & 7
+
+
+def _decode_bias8(codes):  # the other FP8 variant's exponent bias
+    s, e, m = _e4m3_parts(codes)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -7), np.ldexp(1.0 + m / 8.0, e - 8))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _decode_subnormal_exp(codes):  # subnormals scaled by 2^-7 instead of 2^-6
+    s, e, m = _e4m3_parts(codes)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -7), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _decode_mantissa16(codes):  # mantissa step 1/16
+    s, e, m = _e4m3_parts(codes)
+    mag = np.where(e == 0, np.ldexp(m / 16.0, -6), np.ldexp(1.0 + m / 16.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _decode_no_nan(codes):  # treats S.1111.111 as 480
+    s, e, m = _e4m3_parts(codes)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where(s == 1, -mag, mag)
+
+
+def _dequantize_ignores_descale(codes, descale):
+    return of8.decode_e4m3(codes)
+
+
+def _dequantize_squared(codes, descale):
+    return of8.decode_e4m3(codes) * np.float64(np.float32(descale)) ** 2
+
+
+def _pin_fp8_decode_torch():
+    from tests.test_oracle_fp8 import test_decode_matches_torch_all_codes
+    test_decode_matches_torch_all_codes()
+
+
+def _pin_fp8_sdpa():
+    from tests.test_oracle_fp8 import test_fp8_attention_matches_torch_sdpa
+    test_fp8_attention_matches_torch_sdpa(True)
+
+
+MUTATIONS_FP8 = [
+    ("decode_e4m3", _decode_bias8, _pin_fp8_decode_torch),
+    ("decode_e4m3", _decode_subnormal_exp, _pin_fp8_decode_torch),
+    ("decode_e4m3", _decode_mantissa16, _pin_fp8_decode_torch),
+    ("decode_e4m3", _decode_no_nan, _pin_fp8_decode_torch),
+    ("decode_e4m3", _decode_bias8, _pin_fp8_sdpa),
+    ("dequantize", _dequantize_ignores_descale, _pin_fp8_sdpa),
+    ("dequantize", _dequantize_squared, _pin_fp8_sdpa),
+]
+
+
 MUTATIONS = [
     ("scores", _no_scale_scores, lambda: _pin_torch_sdpa(False)),
     ("scores", _shifted_mask_scores, _pin_causal_row0),
@@ -114,5 +176,14 @@ MUTATIONS = [
 def test_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
     pin()  # the unmodified oracle passes the pin
     monkeypatch.setattr(oa, target, bad)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+@pytest.mark.parametrize("target,bad,pin", MUTATIONS_FP8,
+                         ids=[f"{m[1].__name__}-{m[2].__name__}" for m in MUTATIONS_FP8])
+def test_fp8_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
+    pin()
+    monkeypatch.setattr(of8, target, bad)
     with pytest.raises(AssertionError):
         pin()
