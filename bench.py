@@ -32,9 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_launch.h", "fa_fwd.hip", "fa_bwd.hip"]
+KERNEL_SOURCES = ["fa_common.h", "fa_launch.h", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip"]
 
 
 def parse_args():
@@ -49,6 +50,9 @@ def parse_args():
                     help="also time the forward on small-grid shapes (c2's, and few heads with "
                          "long sequences) plain and split-KV with this many key ranges "
                          "(0 = skip); reported under 'splitkv'")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the FP8 (E4M3) forward next to the bf16 forward on the\n"
+                         "fwd+bwd and long-context shapes; reported under 'fp8_forward'")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters); not timed")
@@ -150,6 +154,51 @@ def splitkv_measure(fa, make_inputs, splits: int, iters: int = 20) -> list:
                     "num_splits": splits, "plain_ms": round(plain, 4),
                     "split_ms": round(split, 4), "plain_tflops": round(f / plain / 1e9, 2),
                     "split_tflops": round(f / split / 1e9, 2)})
+    return out
+
+
+# FP8 forward shapes (B, H, N, d, causal, seed): the fwd+bwd workload's and
+# the long-context workload's shapes.
+FP8_SHAPES = [(4, 16, 4096, 128, True, 5100), (1, 16, 16384, 128, True, 4100)]
+
+
+def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
+    """FP8 forward next to the bf16 forward on the same shapes, timed with
+    HIP events on the current stream (average over `iters` launches)."""
+    import numpy as np
+    import torch
+    out = []
+    stream = torch.cuda.current_stream()
+
+    def avg(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for B, H, N, d, causal, seed in FP8_SHAPES:
+        x8 = make_inputs_fp8(B, H, N, d, seed=seed)
+        q8, k8, v8 = (torch.from_numpy(x8[n]).cuda().contiguous() for n in ("q", "k", "v"))
+        x = make_inputs(B, H, N, d, seed=seed)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(
+            torch.bfloat16).cuda() for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        t8 = avg(lambda: fa.flash_attn_fwd_fp8(q8, k8, v8, x8["descale_q"], x8["descale_k"],
+                                               x8["descale_v"], causal=causal, out=o, lse=lse))
+        t16 = avg(lambda: fa.flash_attn_fwd(q, k, v, causal=causal, out=o, lse=lse))
+        f = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        out.append({"shape": f"{'causal' if causal else 'full'} fwd B={B} H={H} N={N} d={d}",
+                    "fp8_ms": round(t8, 4), "fp8_tflops": round(f / t8 / 1e9, 2),
+                    "fp8_frac_of_fp8_peak": round(f / t8 / 1e9 / PEAK_FP8_TFLOPS, 4),
+                    "bf16_ms": round(t16, 4), "bf16_tflops": round(f / t16 / 1e9, 2),
+                    "speedup": round(t16 / t8, 3)})
     return out
 
 
@@ -288,6 +337,9 @@ def main() -> int:
     }
     if args.splitkv > 0:
         line["splitkv"] = splitkv_measure(fa, make_inputs, args.splitkv)
+    if args.fp8:
+        from exact_attention_flash_amd.inputs import make_inputs_fp8
+        line["fp8_forward"] = fp8_measure(fa, make_inputs, make_inputs_fp8)
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(x, wl, causal, args.cpu_heads)
     print(json.dumps(line), flush=True)

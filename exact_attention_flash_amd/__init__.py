@@ -9,6 +9,7 @@ is opened on the first call.
 __all__ = [
     "flash_attn_fwd",
     "flash_attn_fwd_splitkv",
+    "flash_attn_fwd_fp8",
     "flash_attn_fwd_splitkv_workspace_bytes",
     "flash_attn_bwd",
     "flash_attn_bwd_workspace_bytes",

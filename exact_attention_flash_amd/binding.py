@@ -64,6 +64,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.flash_attn_fwd_splitkv.restype = ci
         lib.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         lib.flash_attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.flash_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, fl,
+                                           fl, fl, fl, vp]
+        lib.flash_attn_fwd_fp8.restype = ci
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -79,15 +82,15 @@ def _check(status: int) -> None:
         raise FlashAttnError(status, flash_attn_status_string(status))
 
 
-def _check_tensors(*ts: torch.Tensor, names: str) -> tuple:
+def _check_tensors(*ts: torch.Tensor, names: str, dtypes=(torch.bfloat16,)) -> tuple:
     ref = ts[0]
     if ref.dim() != 4:
         raise ValueError(f"{names.split(',')[0]} must be [B, H, N, d]")
     for t, n in zip(ts, names.split(",")):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{n} must be a torch.Tensor")
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{n} must be {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
         if t.shape != ref.shape:
             raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
         if t.device != ref.device or t.device.type != "cuda":
@@ -131,6 +134,39 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
         st = lib.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), B, H, N, d, int(bool(causal)), scale,
                                 _stream_ptr(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def flash_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       descale_q: float, descale_k: float, descale_v: float,
+                       causal: bool = False, softmax_scale: float | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       stream=None):
+    """FP8 forward over E4M3 codes (uint8 or float8_e4m3fn tensors) with
+    per-tensor descales; returns bf16 ``out`` and float32 ``lse``."""
+    B, H, N, d = _check_tensors(q, k, v, names="q,k,v", dtypes=FP8_DTYPES)
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_tensors(out, names="out")
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must be a bfloat16 tensor of q's shape on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, N, d, int(bool(causal)), scale,
+                                    float(descale_q), float(descale_k), float(descale_v),
+                                    _stream_ptr(q.device, stream))
     _check(st)
     return out, lse
 

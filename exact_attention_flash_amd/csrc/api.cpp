@@ -297,6 +297,43 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int flash_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                       float softmax_scale, float descale_q, float descale_k, float descale_v,
+                       void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  for (const float ds : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(ds) || !(ds > 0.f)) return FA_ERR_BAD_DESCALE;
+  // the scale the kernel applies to the scores must itself be usable
+  const float sl2 = float(double(softmax_scale) * double(descale_q) * double(descale_k) *
+                          1.4426950408889634);
+  if (!std::isfinite(sl2) || !(sl2 > 0.f)) return FA_ERR_BAD_DESCALE;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_MISALIGNED;
+  const size_t nb = size_t(B * H * N * d), lb = size_t(B * H * N) * 4;
+  const Range ins[3] = {range_of(q, nb), range_of(k, nb), range_of(v, nb)};
+  const Range outs[2] = {range_of(o, 2 * nb), range_of(lse, lb)};
+  if (any_alias(outs, 2, ins, 3)) return FA_ERR_ALIASING;
+
+  fa::Fp8FwdArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.N = int(N);
+  a.BH = int(B * H);
+  a.scale_log2 = sl2;
+  a.descale_v = descale_v;
+  const hipError_t e = fa::launch_fwd_fp8(a, int(d), causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -309,6 +346,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_ALIASING: return "an output buffer overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 128";
+    case FA_ERR_BAD_DESCALE: return "FP8 descale factors must be finite and > 0";
     default: return "unknown status";
   }
 }

@@ -30,6 +30,20 @@ struct FwdArgs {
   float* lpart = nullptr;
 };
 
+// FP8 forward: Q, K, V are OCP E4M3 codes, each tensor with one dequantisation
+// factor (real value = descale * e4m3(code)).
+struct Fp8FwdArgs {
+  const uint8_t* q;   // E4M3 [B, H, N, d]
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;        // bf16 [B, H, N, d]
+  float* lse;         // fp32 [B, H, N], natural log
+  int N;
+  int BH;
+  float scale_log2;   // softmax_scale * descale_q * descale_k * log2(e), > 0
+  float descale_v;    // > 0
+};
+
 // Query rows per block of the backward key-block pass; the row vectors in
 // the backward workspace are padded to a multiple of it.
 constexpr int kBwdQueryBlock = 64;
@@ -59,6 +73,9 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // Enqueue the split-KV forward: the partial kernel over a.splits key ranges
 // per query block, then the merge kernel that writes O and LSE.
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Enqueue the FP8 forward kernel for head dim d (64 or 128).
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // The three backward stages, each one kernel launch, for head dim d (64 or
 // 128): the row pass, the pass over key blocks (dK, dV) and the pass over

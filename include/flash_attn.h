@@ -68,7 +68,8 @@ enum fa_status {
   FA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the required size */
   FA_ERR_ALIASING = 7,            /* an output overlaps an input or output */
   FA_ERR_HIP = 8,                 /* the HIP runtime rejected a launch */
-  FA_ERR_BAD_SPLITS = 9           /* num_splits outside 1..128 (split-KV forward) */
+  FA_ERR_BAD_SPLITS = 9,          /* num_splits outside 1..128 (split-KV forward) */
+  FA_ERR_BAD_DESCALE = 10         /* an FP8 descale factor is NaN, Inf or <= 0 */
 };
 
 /*
@@ -126,6 +127,35 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v,
  */
 size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
                                               int64_t num_splits);
+
+/*
+ * FP8 forward: the attention of flash_attn_fwd over Q, K, V given as OCP FP8
+ * E4M3 ("E4M3FN": sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN), one byte per element, each tensor with one
+ * float32 dequantisation factor: the real input is descale * e4m3(code).
+ * Low-precision FP8 matrix products are the FlashAttention-3 change listed
+ * in "FlashAttention 系列技术详解" (section on FlashAttention-3).
+ *   q, k, v    : in,  E4M3 codes [B, H, N, d] (uint8 storage)
+ *   o          : out, bf16 [B, H, N, d]
+ *                O = softmax(softmax_scale * dq * dk * Q K^T (masked)) * dv V
+ *   lse        : out, fp32 [B, H, N], natural log, of those scaled scores
+ *   descale_q, descale_k, descale_v : dq, dk, dv; finite and > 0
+ *                (FA_ERR_BAD_DESCALE otherwise)
+ *   causal, softmax_scale, stream   : as flash_attn_fwd
+ * Both products run on the FP8 matrix cores with fp32 accumulation.  Q K^T
+ * is exact products summed in fp32; the probabilities are rounded to E4M3
+ * (relative error <= 2^-4, values below 2^-14 of the row max may round to
+ * 0) before the product with V, so O is accurate to about that rounding;
+ * the row sums, and hence LSE, use the unrounded fp32 probabilities.
+ * Inputs must hold no NaN codes.  Same shapes, alignment (16 bytes for q, k,
+ * v, o), ownership and error rules as flash_attn_fwd.  Deterministic.
+ */
+int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
+                       void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t d,
+                       int causal, float softmax_scale,
+                       float descale_q, float descale_k, float descale_v,
+                       void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape: two fp32

@@ -65,3 +65,62 @@ def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, what: str) -> float:
     rel = err / scale if scale > 0 else err
     assert err <= GRAD_RTOL * scale + 1e-30, f"{what}: max err {err:.3e} = {rel:.3e} x max|ref|"
     return float(rel)
+
+
+# ---------------------------------------------------------------- FP8 forward
+# The FP8 forward rounds the probabilities to E4M3 before the P V product, so
+# O carries that rounding; the bound below is derived from it (the design
+# notes give the derivation).  With p'_j the kernel's scaled probabilities,
+# |e4m3(p') - p'| <= max(2^-4 p', 2^-10), which gives per element
+#   |O_gpu - O| <= 2^-4 (P |V|)_id + 2^-14 sum_{j: P_ij l_i < 2^-10} |V_jd| / l_i
+# (l_i = sum_j exp(S_ij - max_j S_ij)), plus the bf16 rounding of the output
+# and 2^-10 (P |V|) for fp32 accumulation and exp2 rounding.  Since that bound
+# is loose, the root mean square error over the tensor must also stay within
+# 1.25x the RMS predicted for independent, uniformly distributed rounding
+# errors of relative size at most 2^-4 (variance (2^-4 P_ij)^2 / 3 per term,
+# (2^-14 / l_i)^2 / 3 below the normal range): sigma_id^2 = sum_j var_ij V_jd^2.
+FP8_P_REL = 2.0 ** -4
+FP8_RMS_MARGIN = 1.25
+
+
+def fp8_error_terms(q, k, v, scale, causal, rows=None):
+    """Bound terms for dequantised float64 q, k, v of one head ([N, d] each).
+
+    Returns (a_abs, floor, sigma2) for the listed query rows (all rows when
+    ``rows`` is None): a_abs = P |V|, the subnormal floor term and the
+    per-element variance of the rounding model.
+    """
+    import oracle
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = oracle.scores(q[rows], k, scale, causal, rows=rows)
+    _, ell, p = oracle.softmax_rows(s)
+    av = np.abs(v)
+    a_abs = p @ av
+    small = ((p * ell[:, None]) < 2.0 ** -10) & (p > 0)
+    floor = 2.0 ** -14 * (small @ av) / ell[:, None]
+    # per-term error variance: relative rounding of size <= 2^-4, or, below
+    # the normal range, absolute rounding of size <= 2^-14 / l
+    var = np.maximum((FP8_P_REL * p) ** 2, small * (2.0 ** -14 / ell[:, None]) ** 2) / 3.0
+    sigma2 = var @ (v * v)
+    return a_abs, floor, sigma2
+
+
+def check_o_fp8(o_gpu, o_ref, a_abs, floor, sigma2, what="O (fp8)") -> dict:
+    err = np.abs(o_gpu - o_ref)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    bound = (FP8_P_REL + 2.0 ** -10) * a_abs + floor + half_ulp_bf16(o_ref) + 1e-6
+    bad = err > bound
+    assert not np.any(bad), (
+        f"{what}: {int(bad.sum())} elements beyond the E4M3 bound; "
+        f"worst err {err[bad].max():.3e} vs bound {bound[bad].min():.3e}")
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    # bf16 output rounding adds at most half an ulp, uniformly distributed
+    pred = float(np.sqrt(np.mean(sigma2 + half_ulp_bf16(o_ref) ** 2 / 3.0)))
+    assert rms <= FP8_RMS_MARGIN * pred, (
+        f"{what}: RMS error {rms:.3e} > {FP8_RMS_MARGIN} x predicted {pred:.3e}")
+    return {"max_abs_err": float(err.max()), "rms": rms, "rms_pred": pred}
+
+
+def fp8_to_device(codes: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint8 E4M3 codes -> contiguous uint8 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).to(device).contiguous()

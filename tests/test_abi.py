@@ -19,7 +19,7 @@ from exact_attention_flash_amd.binding import LIB_PATH, load_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS = range(10)
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS, DESCALE = range(11)
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                             reason="fake-pointer validation runs only without a GPU")
@@ -37,7 +37,7 @@ def test_library_exports_header_symbols():
                             "flash_attn_bwd_workspace_bytes", "flash_attn_status_string",
                             "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
                             "flash_attn_bwd_q_blocks", "flash_attn_fwd_splitkv",
-                            "flash_attn_fwd_splitkv_workspace_bytes"])
+                            "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_fwd_fp8"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -48,7 +48,7 @@ def test_library_exports_header_symbols():
 
 def test_status_strings():
     lib = load_library()
-    for s in range(10):
+    for s in range(11):
         assert lib.flash_attn_status_string(s) not in (None, b"unknown status")
     assert lib.flash_attn_status_string(99) == b"unknown status"
 
@@ -130,6 +130,36 @@ def test_fwd_splitkv_validation():
     assert _fwd_split(lib, o=3 * A) == ALIAS                 # O on top of V
 
 
+def _fwd_fp8(lib, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, N=16, d=64, causal=0,
+             scale=0.125, dq=0.01, dk=0.02, dv=0.03):
+    return lib.flash_attn_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv, None)
+
+
+@no_gpu
+def test_fwd_fp8_validation():
+    lib = load_library()
+    assert _fwd_fp8(lib, B=0, q=None) == FA_OK                # empty: no-op
+    assert _fwd_fp8(lib, q=None) == NULLP
+    assert _fwd_fp8(lib, N=-3) == SHAPE
+    assert _fwd_fp8(lib, d=32) == HEADDIM
+    assert _fwd_fp8(lib, scale=0.0) == SCALE
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert _fwd_fp8(lib, dq=bad) == DESCALE
+        assert _fwd_fp8(lib, dk=bad) == DESCALE
+        assert _fwd_fp8(lib, dv=bad) == DESCALE
+    assert _fwd_fp8(lib, B=0, dv=-1.0) == DESCALE             # checked even when empty
+    # the product scale * dq * dk must stay a positive finite float
+    assert _fwd_fp8(lib, dq=1e-30, dk=1e-30) == DESCALE
+    assert _fwd_fp8(lib, dq=1e30, dk=1e30) == DESCALE
+    assert _fwd_fp8(lib, v=3 * A + 8) == MISAL
+    # inputs take one byte per element, O two: O right after a 1-byte Q is fine,
+    # O over the second half of its own 2-byte extent is not
+    n = 16 * 64
+    assert _fwd_fp8(lib, q=A, o=A + n) != ALIAS
+    assert _fwd_fp8(lib, q=A + n, o=A) == ALIAS
+    assert _fwd_fp8(lib, lse=4 * A + 2 * n - 16) == ALIAS     # LSE inside O
+
+
 def _bwd(lib, ws_bytes=None, **kw):
     args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
                 ws=10 * A, B=1, H=2, N=16, d=128, causal=1, scale=0.1)
@@ -190,6 +220,7 @@ def test_valid_call_without_device_reports_hip_error():
     lib = load_library()
     assert _fwd(lib) == HIPERR
     assert _fwd_split(lib) == HIPERR
+    assert _fwd_fp8(lib) == HIPERR
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -199,3 +230,9 @@ def test_python_binding_rejects_cpu_tensors():
         flash_attn_fwd(q, q, q)
     with pytest.raises(TypeError):
         flash_attn_fwd(q.float(), q.float(), q.float())
+    from exact_attention_flash_amd import flash_attn_fwd_fp8
+    q8 = torch.zeros(1, 1, 8, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        flash_attn_fwd_fp8(q8, q8, q8, 1.0, 1.0, 1.0)
+    with pytest.raises(TypeError):
+        flash_attn_fwd_fp8(q, q, q, 1.0, 1.0, 1.0)

@@ -1,0 +1,177 @@
+"""Parity of the FP8 (E4M3) forward with the fp64 oracle, through the C ABI.
+
+Inputs are E4M3 codes with per-tensor amax descales from
+``exact_attention_flash_amd.inputs.make_inputs_fp8``; the oracle decodes the
+same codes exactly.  O is held to the bound derived from the kernel's E4M3
+rounding of the probabilities (``gpu_util.check_o_fp8``); LSE, which the
+kernel computes from unrounded probabilities, to the bf16 path's 1e-3; and
+cases where the rounding is exact (all probabilities equal) to the bf16
+path's O bar.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_flash_amd import flash_attn_fwd_fp8
+from exact_attention_flash_amd.inputs import default_scale, make_inputs_fp8
+
+from gpu_util import (bf16_to_f64, check_lse, check_o, check_o_fp8, fp8_error_terms,
+                      fp8_to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(x, causal, scale, **kw):
+    q, k, v = (fp8_to_device(x[n]) for n in ("q", "k", "v"))
+    o, lse = flash_attn_fwd_fp8(q, k, v, x["descale_q"], x["descale_k"], x["descale_v"],
+                                causal=causal, softmax_scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _deq(x):
+    return tuple(oracle.dequantize(x[n], x["descale_" + n]) for n in ("q", "k", "v"))
+
+
+def _check_full(x, o, lse, causal, scale):
+    O_ref, L_ref = oracle.attention_forward_fp8(x["q"], x["k"], x["v"], x["descale_q"],
+                                                x["descale_k"], x["descale_v"], scale, causal)
+    q, k, v = _deq(x)
+    B, H = q.shape[:2]
+    terms = [fp8_error_terms(q[b, h], k[b, h], v[b, h], scale, causal)
+             for b in range(B) for h in range(H)]
+    shape = q.shape
+    a_abs, floor, sig2 = (np.stack([t[i] for t in terms]).reshape(shape) for i in range(3))
+    res = check_o_fp8(bf16_to_f64(o), O_ref, a_abs, floor, sig2)
+    check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
+    return res
+
+
+SMALL_FP8 = [
+    # (B, H, N, d, causal, q_mult)
+    (1, 1, 128, 64, False, 1.0),
+    (1, 1, 1, 64, False, 1.0),
+    (1, 1, 1, 128, True, 1.0),
+    (1, 2, 63, 64, True, 1.0),
+    (2, 1, 127, 128, False, 1.0),
+    (1, 2, 200, 64, True, 1.0),
+    (1, 1, 1000, 128, True, 1.0),
+    (2, 2, 333, 128, False, 1.0),
+    (1, 3, 513, 64, False, 1.0),
+    (1, 1, 256, 128, True, 1.0),
+    # B*H a multiple of 8 (heads grouped per XCD), ragged last query block
+    (2, 4, 600, 128, True, 1.0),
+    (1, 8, 520, 64, False, 1.0),
+    # large logits: Q times 8
+    (1, 2, 300, 128, True, 8.0),
+    (1, 4, 257, 64, False, 8.0),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,q_mult", SMALL_FP8)
+def test_fwd_fp8_small_full_parity(B, H, N, d, causal, q_mult):
+    _say(f"fp8 fwd small B={B} H={H} N={N} d={d} causal={causal} q_mult={q_mult}")
+    x = make_inputs_fp8(B, H, N, d, seed=N * 3 + d + causal, q_mult=q_mult)
+    scale = default_scale(d)
+    o, lse = _run(x, causal, scale)
+    res = _check_full(x, o, lse, causal, scale)
+    _say(f"  max err {res['max_abs_err']:.3e} rms {res['rms']:.3e} (model {res['rms_pred']:.3e})")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_equal_probabilities(d, causal):
+    """Q = 0: every visible key has the same probability, which E4M3 holds
+    exactly, so O is the (prefix) mean of the dequantised V to bf16
+    rounding and LSE = ln(#visible keys)."""
+    _say(f"fp8 fwd Q=0 d={d} causal={causal}")
+    N = 300
+    x = make_inputs_fp8(1, 2, N, d, seed=21)
+    x["q"][:] = 0
+    scale = default_scale(d)
+    o, lse = _run(x, causal, scale)
+    v = oracle.dequantize(x["v"], x["descale_v"])
+    counts = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = (np.cumsum(v, axis=2) / counts[:, None]) if causal else \
+        np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    check_o(bf16_to_f64(o), mean, "O (Q = 0)")
+    check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(counts), (1, 2, N)))
+
+
+def test_fwd_fp8_descales():
+    """O scales with descale_v exactly (a power of two commutes with the
+    bf16 rounding); only the product descale_q * descale_k matters."""
+    _say("fp8 fwd descale identities")
+    x = make_inputs_fp8(2, 2, 400, 128, seed=31)
+    scale = default_scale(128)
+    o1, l1 = _run(x, True, scale)
+    y = dict(x, descale_v=2 * x["descale_v"])
+    o2, l2 = _run(y, True, scale)
+    assert torch.equal(o2.float(), 2 * o1.float()) and torch.equal(l1, l2)
+    z = dict(x, descale_q=x["descale_k"], descale_k=x["descale_q"])
+    o3, l3 = _run(z, True, scale)
+    assert torch.equal(o3.view(torch.int16), o1.view(torch.int16)) and torch.equal(l3, l1)
+
+
+def test_fwd_fp8_deterministic():
+    x = make_inputs_fp8(2, 3, 777, 128, seed=5)
+    o1, l1 = _run(x, True, default_scale(128))
+    o2, l2 = _run(x, True, default_scale(128))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_fwd_fp8_accepts_float8_dtype_and_out_buffers():
+    x = make_inputs_fp8(1, 2, 130, 64, seed=7)
+    o1, l1 = _run(x, False, 0.125)
+    q, k, v = (fp8_to_device(x[n]).view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
+    out = torch.full_like(o1, float("nan"))
+    lse = torch.full_like(l1, float("nan"))
+    flash_attn_fwd_fp8(q, k, v, x["descale_q"], x["descale_k"], x["descale_v"],
+                       softmax_scale=0.125, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o1.view(torch.int16)) and torch.equal(lse, l1)
+
+
+# Full-size shapes of the long-context and fwd+bwd workloads, in FP8, in the
+# configuration the bench times; compared on sampled rows of sampled heads.
+FULL_FP8 = [
+    # (name, B, H, N, d, causal, seed)
+    ("c4-fp8", 1, 16, 16384, 128, True, 4100),
+    ("c5-fp8", 4, 16, 4096, 128, True, 5100),
+    ("c3-fp8", 16, 12, 1024, 64, False, 3100),
+]
+
+
+@pytest.mark.parametrize("name,B,H,N,d,causal,seed", FULL_FP8)
+def test_fwd_fp8_full_size_sampled(name, B, H, N, d, causal, seed):
+    _say(f"fp8 fwd full size {name}: B={B} H={H} N={N} d={d} causal={causal}")
+    x = make_inputs_fp8(B, H, N, d, seed=seed)
+    scale = default_scale(d)
+    o, lse = _run(x, causal, scale)
+    o_all = o.float()
+    assert bool(torch.isfinite(o_all).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(seed)
+    heads = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, N - 257, N - 2, N - 1],
+                                     rng.integers(0, N, 25)]))
+    for b, h in heads:
+        xs = {n: x[n][b, h] for n in ("q", "k", "v")}
+        O_ref, L_ref = oracle.attention_forward_fp8_rows(
+            xs["q"], xs["k"], xs["v"], x["descale_q"], x["descale_k"], x["descale_v"],
+            scale, causal, rows)
+        q = oracle.dequantize(xs["q"], x["descale_q"])
+        k = oracle.dequantize(xs["k"], x["descale_k"])
+        v = oracle.dequantize(xs["v"], x["descale_v"])
+        a_abs, floor, sig2 = fp8_error_terms(q, k, v, scale, causal, rows)
+        og = bf16_to_f64(o[b, h][torch.as_tensor(rows, device=o.device)])
+        check_o_fp8(og, O_ref, a_abs, floor, sig2, f"O (fp8) head {b},{h}")
+        check_lse(lse[b, h].cpu().numpy()[rows].astype(np.float64), L_ref)
