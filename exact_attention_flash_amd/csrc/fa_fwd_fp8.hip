@@ -22,8 +22,11 @@
 // gfx950 mapping: the ping-pong structure of the bf16 forward (one workgroup
 // = 8 waves = 256 query rows, 32 per wave; waves w and w + 4 share a SIMD
 // and alternate a matrix phase with a softmax phase, half a period apart),
-// with 8 KB tiles of BC = 8192 / d keys (64 for d = 128, 128 for d = 64) in
-// three K and three V buffers.  MFMA operands (lane l = 32 g + c):
+// with tiles of BC = 128 keys (16 KB for d = 128, 8 KB for d = 64) in three
+// K and three V buffers; the larger tile than the bf16 kernel's halves the
+// per-key cost of the period's fixed work (barriers, branches, copy issue),
+// which matters here because the softmax phase, not the matrix phase, sets
+// the period.  MFMA operands (lane l = 32 g + c):
 //  * A (K rows): lane (c, g) holds 32 bytes of row c; B (Q^T): lane holds 32
 //    bytes of its query's row; byte j of the A lane pairs with byte j of the
 //    B lane of the same g (measured: any k order shared by both operands
@@ -71,9 +74,11 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 }
 
 // Four fp32 values rounded to E4M3 (nearest even) into the bytes of one
-// word, a in byte 0 .. d in byte 3.
+// word, a in byte 0 .. d in byte 3.  The first conversion keeps bytes 2-3 of
+// its `old` operand, which the second one overwrites, so any register does
+// (here a's own, which needs no copy).
 __device__ __forceinline__ int cvt_e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -83,14 +88,15 @@ struct Fp8Cfg {
   static constexpr int NT = NW * 64;            // threads per workgroup
   static constexpr int QW = 32;                 // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per workgroup
-  static constexpr int BC = 8192 / D;           // keys per K/V tile (8 KB)
+  static constexpr int BC = 128;                // keys per K/V tile
   static constexpr int CPR = D / 16;            // 16-byte chunks per row
   static constexpr int TILE = BC * D;           // bytes per tile
+  static constexpr int COPIES = TILE / 16 / NT; // 16-byte copies per thread per tile
   static constexpr int KS = D / 64;             // 64-deep slices of S^T = K Q^T
   static constexpr int SB = BC / 32;            // 32-key blocks of S^T
   static constexpr int PS = BC / 64;            // 64-key slices of O^T += V^T P^T
   static constexpr int DB = D / 32;             // 32-column blocks of O^T
-  static_assert(TILE / 16 == NT, "one 16-byte copy per thread per tile");
+  static_assert(COPIES >= 1 && COPIES * 16 * NT == TILE, "tile copies must split evenly");
 };
 
 // Growth of the probabilities (log2 units) tolerated before the running max
@@ -117,25 +123,39 @@ __device__ __forceinline__ int fp8_v_swizzle(int r) {
 template <int D>
 struct Fp8TileCopy {
   using C = Fp8Cfg<D>;
-  uint32_t koff, voff;
+  uint32_t koff[C::COPIES], voff[C::COPIES];
+
+  __device__ __forceinline__ static int slot_row(int t, int w, int lane) {
+    return ((t * C::NW + w) * 64 + lane) / C::CPR;
+  }
 
   __device__ __forceinline__ void init(int w, int lane) {
-    const int slot = w * 64 + lane;
-    const int r = slot / C::CPR, pc = slot % C::CPR;
-    koff = r * D + 16 * (pc ^ fp8_k_swizzle<D>(r));
-    voff = r * D + 16 * (pc ^ (fp8_v_swizzle<D>(r) << 1));
+#pragma unroll
+    for (int t = 0; t < C::COPIES; ++t) {
+      const int slot = (t * C::NW + w) * 64 + lane;
+      const int r = slot / C::CPR, pc = slot % C::CPR;
+      koff[t] = r * D + 16 * (pc ^ fp8_k_swizzle<D>(r));
+      voff[t] = r * D + 16 * (pc ^ (fp8_v_swizzle<D>(r) << 1));
+    }
   }
 
   template <bool KEYS>
   __device__ __forceinline__ void issue(const uint8_t* X, uint8_t* Ts, int k0, int N, int w,
                                         int lane) const {
     const i32x4 rs = make_rsrc_words(X + (int64_t)k0 * D, C::TILE);
-    uint32_t off = KEYS ? koff : voff;
-    if (k0 + C::BC > N) {
-      const int r = opaque((w * 64 + lane) / C::CPR);
-      off += (uint32_t)((min(k0 + r, N - 1) - (k0 + r)) * D);
+    if (k0 + C::BC <= N) {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t)
+        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + (t * C::NW + w) * 64 * 16);
+    } else {
+#pragma unroll
+      for (int t = 0; t < C::COPIES; ++t) {
+        const int r = opaque(slot_row(t, w, lane));
+        const uint32_t shift = (uint32_t)((min(k0 + r, N - 1) - (k0 + r)) * D);
+        buffer_load_lds16_unseen(rs, (KEYS ? koff[t] : voff[t]) + shift,
+                                 Ts + (t * C::NW + w) * 64 * 16);
+      }
     }
-    buffer_load_lds16_unseen(rs, off, Ts + w * 64 * 16);
   }
 };
 
@@ -228,11 +248,14 @@ struct Fp8Wave {
         for (int i = 0; i < 16; ++i)
           if (32 * sb + 8 * (i >> 2) + (i & 3) > lim) s[sb][i] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // row max in four independent chains (a single chain of dependent
+    // v_max3 is latency bound)
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+      for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], s[sb][i]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = max_halves(mx) * sl2;
     if (__ballot(mx > m_run + kFp8RescaleThreshold)) {
       const float m_new = fmaxf(m_run, mx);
@@ -263,7 +286,7 @@ struct Fp8Wave {
   }
 
   // One period of the ping-pong schedule; see the bf16 forward for the
-  // buffer rotation.  One 16-byte copy per lane per tile.
+  // buffer rotation.
   template <int R, int GRP>
   __device__ __forceinline__ void period(int t) {
     constexpr int KB = R, VB = (R + 2) % 3, KN = (R + 2) % 3, VN = (R + 1) % 3;
@@ -283,8 +306,8 @@ struct Fp8Wave {
     } else {
       matrix_phase<KB, VB>(t);
     }
-    if (kn) wait_vmem_except_last<2>();
-    else if (vn) wait_vmem_except_last<1>();
+    if (kn) wait_vmem_except_last<2 * C::COPIES>();
+    else if (vn) wait_vmem_except_last<C::COPIES>();
     else wait_vmem();
     block_barrier();
   }
@@ -339,6 +362,7 @@ fa_fwd_fp8_kernel(Fp8FwdArgs a) {
   f.t0 = 0;
   f.nt = nt_all;
   f.ntw = CAUSAL ? min(nt_all, (f.qw0 + C::QW + C::BC - 1) / C::BC) : nt_all;
+  asm volatile("" : "+s"(f.ntw));  // keep the per-tile tests: knowing ntw == nt hoists more
   f.sl2 = a.scale_log2;
   f.m_run = -INFINITY;
   f.l_part = 0.f;
