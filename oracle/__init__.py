@@ -21,6 +21,10 @@ Sources (the web pages this method is described on):
 * "FlashAttention 系列技术详解", FlashAttention-3 section: FP8 matrix
   products.  ``fp8`` decodes OCP E4M3 inputs (format from the OCP 8-bit
   floating point specification) and runs the same exact attention on them.
+* "FlashAttention 的基本原理", section 2.4 (the backward algorithm also covers
+  dropout) and the apxml example (dropout on the attention weights):
+  ``dropout`` draws the keep mask with Philox4x32-10 (Salmon et al., SC 2011)
+  and gives the forward and the gradients with the mask applied.
 
 Every function names the passage it follows.  All arithmetic is float64.
 
@@ -46,6 +50,16 @@ from .fp8 import (
     attention_forward_fp8,
     attention_forward_fp8_rows,
 )
+from .dropout import (
+    philox,
+    dropout_threshold,
+    dropout_scale,
+    dropout_bytes,
+    dropout_mask,
+    attention_forward_dropout,
+    attention_forward_dropout_rows,
+    attention_backward_dropout,
+)
 from .online_softmax import (
     softmax_stats,
     merge_stats,
@@ -66,6 +80,14 @@ __all__ = [
     "dequantize",
     "attention_forward_fp8",
     "attention_forward_fp8_rows",
+    "philox",
+    "dropout_threshold",
+    "dropout_scale",
+    "dropout_bytes",
+    "dropout_mask",
+    "attention_forward_dropout",
+    "attention_forward_dropout_rows",
+    "attention_backward_dropout",
     "softmax_stats",
     "merge_stats",
     "fold_blocks",

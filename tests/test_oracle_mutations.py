@@ -187,3 +187,128 @@ def test_fp8_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
     monkeypatch.setattr(of8, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ---------------------------------------------------------------- dropout
+import oracle.dropout as odr
+
+
+def _philox_swapped_multipliers(counter, key, width=32, rounds=10):
+    M0, M1, W0, W1 = odr.PHILOX[width]
+    mask = (1 << width) - 1
+    x = [int(v) & mask for v in counter]
+    k = [int(v) & mask for v in key]
+    for _ in range(rounds):
+        p0 = M1 * x[0]
+        p1 = M0 * x[2]
+        x = [((p1 >> width) ^ x[1] ^ k[0]) & mask, p1 & mask,
+             ((p0 >> width) ^ x[3] ^ k[1]) & mask, p0 & mask]
+        k = [(k[0] + W0) & mask, (k[1] + W1) & mask]
+    return x
+
+
+def _philox_seven_rounds(counter, key, width=32, rounds=10):
+    return _REAL_PHILOX(counter, key, width, 7)
+
+
+def _philox_key_bumped_first(counter, key, width=32, rounds=10):
+    M0, M1, W0, W1 = odr.PHILOX[width]
+    mask = (1 << width) - 1
+    k = [(int(key[0]) + W0) & mask, (int(key[1]) + W1) & mask]
+    return _REAL_PHILOX(counter, k, width, rounds)
+
+
+_REAL_PHILOX = odr.philox
+_REAL_BYTES = odr.dropout_bytes
+_REAL_ARRAY = odr.philox4x32_10_array
+
+
+def _bytes_big_endian(seed, offset, bh, rows, N):
+    rows = np.asarray(rows, dtype=np.int64)
+    ng = (N + 15) // 16
+    jg = np.arange(ng, dtype=np.int64)
+    w = odr.philox4x32_10_array(jg[None, :], rows[:, None], bh, offset,
+                                seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    return w.astype(">u4").view(np.uint8).reshape(len(rows), ng * 16)[:, :N]
+
+
+def _bytes_counter_swapped(seed, offset, bh, rows, N):
+    rows = np.asarray(rows, dtype=np.int64)
+    ng = (N + 15) // 16
+    jg = np.arange(ng, dtype=np.int64)
+    w = odr.philox4x32_10_array(rows[:, None], jg[None, :], bh, offset,
+                                seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    return w.astype("<u4").view(np.uint8).reshape(len(rows), ng * 16)[:, :N]
+
+
+def _mask_strict(seed, offset, bh, rows, N, p):
+    return _REAL_BYTES(seed, offset, bh, rows, N) > odr.dropout_threshold(p)
+
+
+def _scale_keep_rate_inverted(p):
+    return (256 - odr.dropout_threshold(p)) / 256.0
+
+
+def _backward_no_mask_in_dp(q, k, v, dout, scale, causal, p, seed, offset=0):
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, H, N, d = q.shape
+    s = odr.dropout_scale(p)
+    dQ, dK, dV = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            P = oa.softmax_rows(oa.scores(q[b, h], k[b, h], scale, causal))[2]
+            Zs = odr.dropout_mask(seed, offset, b * H + h, np.arange(N), N, p) * s
+            dV[b, h] = (P * Zs).T @ do[b, h]
+            dS = oa.softmax_row_grad(P, do[b, h] @ v[b, h].T)
+            dQ[b, h] = scale * (dS @ k[b, h])
+            dK[b, h] = scale * (dS.T @ q[b, h])
+    return dQ, dK, dV
+
+
+def _pin_numpy_philox():
+    from tests.test_oracle_dropout import test_philox4x64_matches_numpy
+    test_philox4x64_matches_numpy([5, 0, 0, 0], [7, 9])
+
+
+def _pin_layout():
+    from tests.test_oracle_dropout import test_bytes_and_mask_layout
+    test_bytes_and_mask_layout()
+
+
+def _pin_brute(causal=True):
+    from tests.test_oracle_dropout import test_forward_brute_force
+    test_forward_brute_force(causal)
+
+
+def _pin_stats():
+    from tests.test_oracle_dropout import test_mask_statistics
+    test_mask_statistics()
+
+
+def _pin_autograd():
+    from tests.test_oracle_dropout import test_backward_torch_autograd
+    test_backward_torch_autograd(True)
+
+
+MUTATIONS_DROPOUT = [
+    ("philox", _philox_swapped_multipliers, _pin_numpy_philox),
+    ("philox", _philox_seven_rounds, _pin_numpy_philox),
+    ("philox", _philox_key_bumped_first, _pin_numpy_philox),
+    ("dropout_bytes", _bytes_big_endian, _pin_layout),
+    ("dropout_bytes", _bytes_counter_swapped, _pin_layout),
+    ("dropout_bytes", _bytes_big_endian, _pin_brute),
+    ("dropout_mask", _mask_strict, _pin_stats),
+    ("dropout_scale", _scale_keep_rate_inverted, _pin_brute),
+    ("attention_backward_dropout", _backward_no_mask_in_dp, _pin_autograd),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", MUTATIONS_DROPOUT,
+                         ids=[f"{m[1].__name__}-{m[2].__name__}" for m in MUTATIONS_DROPOUT])
+def test_dropout_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
+    pin()
+    monkeypatch.setattr(odr, target, bad)
+    if target == "attention_backward_dropout":
+        monkeypatch.setattr(oracle, target, bad)
+    with pytest.raises(AssertionError):
+        pin()
