@@ -10,6 +10,8 @@ __all__ = [
     "flash_attn_fwd",
     "flash_attn_fwd_splitkv",
     "flash_attn_fwd_fp8",
+    "flash_attn_fwd_dropout",
+    "flash_attn_bwd_dropout",
     "flash_attn_fwd_splitkv_workspace_bytes",
     "flash_attn_bwd",
     "flash_attn_bwd_workspace_bytes",

@@ -67,6 +67,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.flash_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, fl,
                                            fl, fl, fl, vp]
         lib.flash_attn_fwd_fp8.restype = ci
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.flash_attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, fl,
+                                               fl, u64, u32, vp]
+        lib.flash_attn_fwd_dropout.restype = ci
+        lib.flash_attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_size_t, i64, i64, i64, i64, ci, fl,
+                                               fl, u64, u32, vp]
+        lib.flash_attn_bwd_dropout.restype = ci
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -236,6 +244,75 @@ def flash_attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torc
                                 lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                 dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
                                 int(bool(causal)), scale, _stream_ptr(q.device, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def _seed_offset(seed: int, offset: int) -> tuple:
+    seed, offset = int(seed), int(offset)
+    if not 0 <= seed < 2**64 or not 0 <= offset < 2**32:
+        raise ValueError("seed must fit 64 bits and offset 32 bits (unsigned)")
+    return seed, offset
+
+
+def flash_attn_fwd_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dropout_p: float,
+                           seed: int, offset: int = 0, causal: bool = False,
+                           softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                           lse: torch.Tensor | None = None, stream=None):
+    """O = (P o Z s) V with the Philox keep mask Z of (seed, offset); returns ``(out, lse)``."""
+    B, H, N, d = _check_tensors(q, k, v, names="q,k,v")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    seed, offset = _seed_offset(seed, offset)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out, names="q,out")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), B, H, N, d, int(bool(causal)), scale,
+                                        float(dropout_p), seed, offset,
+                                        _stream_ptr(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_bwd_dropout(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           out: torch.Tensor, lse: torch.Tensor, dropout_p: float, seed: int,
+                           offset: int = 0, causal: bool = False,
+                           softmax_scale: float | None = None, dq: torch.Tensor | None = None,
+                           dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None):
+    """dQ, dK, dV of flash_attn_fwd_dropout with the same (dropout_p, seed, offset)."""
+    B, H, N, d = _check_tensors(q, k, v, out, dout, names="q,k,v,out,dout")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    seed, offset = _seed_offset(seed, offset)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensors(q, dq, dk, dv, names="q,dq,dk,dv")
+    lib = load_library()
+    need = int(lib.flash_attn_bwd_workspace_bytes(B, H, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                        ws_bytes, B, H, N, d, int(bool(causal)), scale,
+                                        float(dropout_p), seed, offset,
+                                        _stream_ptr(q.device, stream))
     _check(st)
     return dq, dk, dv
 

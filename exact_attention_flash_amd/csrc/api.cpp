@@ -44,6 +44,20 @@ int check_scale(float s) {
   return FA_OK;
 }
 
+// Dropout threshold t = floor(256 p + 1/2), 0 <= t <= 255, and the rescale
+// 256 / (256 - t); FA_ERR_BAD_DROPOUT for NaN, negative or too large p.
+int prepare_dropout(float p, uint64_t seed, uint32_t offset, fa::DropArgs* d) {
+  if (!(p >= 0.f)) return FA_ERR_BAD_DROPOUT;  // also NaN
+  const double t = std::floor(256.0 * double(p) + 0.5);
+  if (!(t <= 255.0)) return FA_ERR_BAD_DROPOUT;
+  d->t = uint32_t(t);
+  d->scale = float(256.0 / (256.0 - t));
+  d->k0 = uint32_t(seed);
+  d->k1 = uint32_t(seed >> 32);
+  d->offset = offset;
+  return FA_OK;
+}
+
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
@@ -155,16 +169,16 @@ int prepare_bwd(const BwdPtrs& p, unsigned used, size_t workspace_bytes, int64_t
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                   int64_t H, int64_t N, int64_t d, int causal, float softmax_scale, void* stream) {
+// Shared by flash_attn_fwd and flash_attn_fwd_dropout: validation and the
+// argument block.  Returns FA_OK with a->BH == 0 for an empty problem.
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t H, int64_t N, int64_t d, float softmax_scale, const fa::DropArgs* drop,
+                fa::FwdArgs* a) {
   bool empty = false;
   int st = check_shape(B, H, N, d, &empty);
   if (st != FA_OK) return st;
   if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  a->BH = 0;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -173,16 +187,47 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
   const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
   const Range outs[2] = {range_of(o, tb), range_of(lse, lb)};
   if (any_alias(outs, 2, ins, 3)) return FA_ERR_ALIASING;
+  a->q = static_cast<const uint16_t*>(q);
+  a->k = static_cast<const uint16_t*>(k);
+  a->v = static_cast<const uint16_t*>(v);
+  a->o = static_cast<uint16_t*>(o);
+  a->lse = lse;
+  a->N = int(N);
+  a->BH = int(B * H);
+  a->scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (drop) a->drop = *drop;
+  return FA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+
+int flash_attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                           float softmax_scale, float dropout_p, uint64_t seed, uint32_t offset,
+                           void* stream) {
+  fa::DropArgs drop;
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if ((st = prepare_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
   fa::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.N = int(N);
-  a.BH = int(B * H);
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if ((st = prepare_fwd(q, k, v, o, lse, B, H, N, d, softmax_scale, &drop, &a)) != FA_OK ||
+      a.BH == 0)
+    return st;
+  const hipError_t e =
+      fa::launch_fwd_dropout(a, int(d), causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                   int64_t H, int64_t N, int64_t d, int causal, float softmax_scale, void* stream) {
+  fa::FwdArgs a;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, N, d, softmax_scale, nullptr, &a);
+  if (st != FA_OK || a.BH == 0) return st;
   const hipError_t e = fa::launch_fwd(a, int(d), causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -334,6 +379,29 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, flo
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int flash_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float softmax_scale, float dropout_p,
+                           uint64_t seed, uint32_t offset, void* stream) {
+  fa::DropArgs drop;
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if ((st = prepare_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
+  const BwdPtrs p{q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  fa::BwdArgs a;
+  st = prepare_bwd(p, kAllBwd, workspace_bytes, B, H, N, d, softmax_scale, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  a.drop = drop;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fa::launch_bwd_pre(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_kv_dropout(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_q_dropout(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -347,6 +415,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 128";
     case FA_ERR_BAD_DESCALE: return "FP8 descale factors must be finite and > 0";
+    case FA_ERR_BAD_DROPOUT: return "dropout_p must be >= 0 and round (in steps of 1/256) below 1";
     default: return "unknown status";
   }
 }

@@ -126,6 +126,7 @@ struct KvSmem {
   uint16_t* q[2];
   uint16_t* dout[2];
   float* vec[2];
+  uint8_t* drop;  // dropout bytes, 1 KiB per wave (DROP only)
 };
 
 // One workgroup of the key-block pass (8 waves, 16 keys each).  S = Q K^T,
@@ -133,14 +134,14 @@ struct KvSmem {
 // with a lane owning one key; the 16 queries of an S tile are fed in the
 // order that gives each lane 8 consecutive queries per 32-query group, so P
 // and dS are directly the B operands of the dV and dK products.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 struct KvBlock {
   using C = KvCfg<D>;
   static constexpr int BRQ = C::BRQ, BCK = C::BCK;
 
   const KvSmem sm;
   const BwdArgs& a;
-  int w, lane, c16, kg, N, kb0, kw0, key, nqb;
+  int w, lane, c16, kg, N, kb0, kw0, key, nqb, bh;
   int64_t hoff;
   const uint16_t* Qh;
   const uint16_t* dOh;
@@ -154,7 +155,7 @@ struct KvBlock {
   f32x4 dk[D / 16], dv[D / 16];   // dK^T, dV^T: lane holds [16 dt + 4 kg + i][key]
 
   __device__ __forceinline__ KvBlock(const KvSmem& sm_, const BwdArgs& a_, int bh, int kb0_)
-      : sm(sm_), a(a_) {
+      : sm(sm_), a(a_), bh(bh) {
     const int tid = threadIdx.x;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     lane = tid & 63;
@@ -209,6 +210,24 @@ struct KvBlock {
     }
   }
 
+  // Dropout bytes of this lane's key for the block's queries: byte m of the
+  // result belongs to query q0 + 32 (m / 8) + 8 kg + m % 8.  The wave's 16
+  // keys are one 16-key group of the Philox layout, so the call for one
+  // query gives the bytes of all 16 keys: lane (c16, kg) draws for query
+  // m = c16 of its kg group, and the 16 x 16 bytes of the group are
+  // transposed through the wave's LDS region (byte b of lane m to row b,
+  // column m; row c16 read back).
+  __device__ __forceinline__ i32x4 drop_bytes(int q0) const {
+    const int m = c16;
+    const uint32_t qd = (uint32_t)(q0 + 32 * (m >> 3) + 8 * kg + (m & 7));
+    const u32x4 r = philox4x32_10((uint32_t)(kw0 >> 4), qd, (uint32_t)bh, a.drop.offset,
+                                  a.drop.k0, a.drop.k1);
+    uint8_t* base = sm.drop + (w * 4 + kg) * 256;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) base[b * 16 + m] = (uint8_t)(r[b >> 2] >> (8 * (b & 3)));
+    return *reinterpret_cast<const i32x4*>(base + c16 * 16);
+  }
+
   // S, P, dP, dS for query block i (stage ST); dV^T and dK^T accumulate.
   template <int ST>
   __device__ __forceinline__ void block(int i) {
@@ -216,6 +235,8 @@ struct KvBlock {
     const uint16_t* dOt = sm.dout[ST];
     const float* lv = sm.vec[ST];
     const int q0 = i * BRQ;
+    i32x4 rb;
+    if constexpr (DROP) rb = drop_bytes(q0);
     const int sb = opaque(srow_base), su = opaque(srow_u);
     const int tb = opaque(tq_base), tt = opaque(tq_t);
 #pragma unroll
@@ -254,8 +275,17 @@ struct KvBlock {
           const int q = q0 + ql + j;
           if (key >= N || (CAUSAL && key > q)) pv = 0.f;
         }
-        p[j] = pv;
-        ds[j] = pv * (dpv - dlt);
+        if constexpr (DROP) {
+          // dV takes the kept probabilities (rescaled at the store); dS the
+          // kept dP, rescaled: dS = P (Z s dP - D)
+          const int mb = 8 * qg + j;
+          const bool keep = drop_keep((uint32_t)rb[mb >> 2], mb & 3, a.drop.t);
+          p[j] = keep ? pv : 0.f;
+          ds[j] = pv * fmaf(dpv, keep ? a.drop.scale : 0.f, -dlt);
+        } else {
+          p[j] = pv;
+          ds[j] = pv * (dpv - dlt);
+        }
       }
       const bf16x8 pb = pack8(p);
       const bf16x8 sbv = pack8(ds);
@@ -293,15 +323,21 @@ struct KvBlock {
       u32x2 kv, vv;
       kv.x = pack2(dk[dt][0] * sc, dk[dt][1] * sc);
       kv.y = pack2(dk[dt][2] * sc, dk[dt][3] * sc);
-      vv.x = pack2(dv[dt][0], dv[dt][1]);
-      vv.y = pack2(dv[dt][2], dv[dt][3]);
+      if constexpr (DROP) {
+        const float vs = a.drop.scale;  // the dropout rescale of the kept P
+        vv.x = pack2(dv[dt][0] * vs, dv[dt][1] * vs);
+        vv.y = pack2(dv[dt][2] * vs, dv[dt][3] * vs);
+      } else {
+        vv.x = pack2(dv[dt][0], dv[dt][1]);
+        vv.y = pack2(dv[dt][2], dv[dt][3]);
+      }
       *reinterpret_cast<u32x2*>(dKrow + col) = kv;
       *reinterpret_cast<u32x2*>(dVrow + col) = vv;
     }
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_bwd_kv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
@@ -312,7 +348,8 @@ fa_bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t do1_s[C::QT];
   __shared__ __attribute__((aligned(16))) float vec0_s[2 * C::BRQ];
   __shared__ __attribute__((aligned(16))) float vec1_s[2 * C::BRQ];
-  const KvSmem sm{{q0_s, q1_s}, {do0_s, do1_s}, {vec0_s, vec1_s}};
+  __shared__ __attribute__((aligned(16))) uint8_t drop_s[DROP ? C::NW * 1024 : 16];
+  const KvSmem sm{{q0_s, q1_s}, {do0_s, do1_s}, {vec0_s, vec1_s}, drop_s};
 
   const int N = a.N;
   const int nkb = (N + C::BCK - 1) / C::BCK;
@@ -322,7 +359,7 @@ fa_bwd_kv_kernel(BwdArgs a) {
   int bh, kb;
   xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nkb, bh, kb);
 
-  KvBlock<D, CAUSAL> blk(sm, a, bh, kb * C::BCK);
+  KvBlock<D, CAUSAL, DROP> blk(sm, a, bh, kb * C::BCK);
   const int nqb = blk.nqb;
   const int i0 = CAUSAL ? blk.kb0 / C::BRQ : 0;
   blk.template issue_q<0>(i0);
@@ -359,11 +396,13 @@ struct QCfg {
 //   dQ^T += K^T dS^T (K^T read transposed from the K tile, dS^T straight
 //   from registers as the B operand).
 // dQ stays in registers and is written once.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 struct QBlock {
   using C = QCfg<D>;
   static constexpr int BC = C::BC;
 
+  DropArgs drop;  // DROP only
+  int bh;
   uint16_t* ks[2];
   uint16_t* vs[2];
   const uint16_t* Kh;
@@ -441,6 +480,22 @@ struct QBlock {
       // keep the K / V reads two slices ahead of the MFMAs that consume them
       sched_pipeline<D / 16, 2 * (BC / 32), 2 * (BC / 32), 2>();
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
+      // dropout bytes of keys 16 n + 8 g + 0..7 (as in the forward pass: the
+      // lane draws 16-key group 2 m + g and swaps half with the other wave half)
+      uint32_t rw[BC / 16][2];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int m = 0; m < BC / 32; ++m) {
+          const u32x4 own = philox4x32_10((uint32_t)(k0 >> 4) + 2 * m + g, (uint32_t)qrow,
+                                          (uint32_t)bh, drop.offset, drop.k0, drop.k1);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(own[e], own[2 + e], false, false);
+            rw[2 * m][e] = r[0];
+            rw[2 * m + 1][e] = r[1];
+          }
+        }
+      }
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
@@ -450,7 +505,12 @@ struct QBlock {
             const int key = k0 + 32 * sb + 16 * (i >> 3) + 8 * g + (i & 7);
             if (key >= N || (CAUSAL && key > qrow)) pv = 0.f;
           }
-          s[sb][i] = pv * (dp[sb][i] - dlt);  // dS^T
+          if constexpr (DROP) {
+            const bool keep = drop_keep(rw[2 * sb + (i >> 3)][(i & 7) >> 2], i & 3, drop.t);
+            s[sb][i] = pv * fmaf(dp[sb][i], keep ? drop.scale : 0.f, -dlt);  // dS^T
+          } else {
+            s[sb][i] = pv * (dp[sb][i] - dlt);  // dS^T
+          }
         }
       // dQ^T += K^T dS^T over the tile's four 16-key chunks.
 #pragma unroll
@@ -472,7 +532,7 @@ struct QBlock {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_bwd_q_kernel(BwdArgs a) {
   using C = QCfg<D>;
@@ -491,7 +551,9 @@ fa_bwd_q_kernel(BwdArgs a) {
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;
-  QBlock<D, CAUSAL> f;
+  QBlock<D, CAUSAL, DROP> f;
+  f.drop = a.drop;
+  f.bh = bh;
   f.ks[0] = k0s;
   f.ks[1] = k1s;
   f.vs[0] = v0s;
@@ -561,21 +623,21 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t stream) {
   using C = KvCfg<D>;
   const int64_t nkb = (a.N + C::BCK - 1) / C::BCK;
-  hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.BH)), dim3(C::NT), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL, DROP>), dim3((unsigned)(nkb * a.BH)), dim3(C::NT),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 static hipError_t launch_q_t(const BwdArgs& a, hipStream_t stream) {
   using C = QCfg<D>;
   const int64_t nqb = (a.N + C::BR - 1) / C::BR;
-  hipLaunchKernelGGL((fa_bwd_q_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.BH)), dim3(C::NT), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fa_bwd_q_kernel<D, CAUSAL, DROP>), dim3((unsigned)(nqb * a.BH)), dim3(C::NT),
+                     0, stream, a);
   return hipGetLastError();
 }
 
@@ -591,6 +653,18 @@ hipError_t launch_bwd_kv(const BwdArgs& a, int d, bool causal, hipStream_t strea
 hipError_t launch_bwd_q(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 64) return causal ? launch_q_t<64, true>(a, stream) : launch_q_t<64, false>(a, stream);
   return causal ? launch_q_t<128, true>(a, stream) : launch_q_t<128, false>(a, stream);
+}
+
+hipError_t launch_bwd_kv_dropout(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_kv_t<64, true, true>(a, stream) : launch_kv_t<64, false, true>(a, stream);
+  return causal ? launch_kv_t<128, true, true>(a, stream) : launch_kv_t<128, false, true>(a, stream);
+}
+
+hipError_t launch_bwd_q_dropout(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_q_t<64, true, true>(a, stream) : launch_q_t<64, false, true>(a, stream);
+  return causal ? launch_q_t<128, true, true>(a, stream) : launch_q_t<128, false, true>(a, stream);
 }
 
 }  // namespace fa

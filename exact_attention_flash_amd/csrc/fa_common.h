@@ -482,3 +482,38 @@ __device__ __forceinline__ int qtile_swizzle(int row) {
 }
 
 }  // namespace fa
+
+namespace fa {
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of
+//   (x0, x1, x2, x3) -> (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0))
+// with the key advanced by the Weyl increments after every round.  The key
+// is wave-uniform, so its schedule stays in scalar registers; each 32 x 32-bit
+// product is one v_mad_u64_u32.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                               uint32_t k0, uint32_t k1) {
+  // recompute the round keys at each call instead of keeping all twenty
+  // hoisted in scalar registers
+  asm volatile("" : "+s"(k0), "+s"(k1));
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    x0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    x1 = (uint32_t)p1;
+    x2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    x3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  u32x4 r = {x0, x1, x2, x3};
+  return r;
+}
+
+// Byte b (0..3) of word w, compared with the dropout threshold: kept iff >= t.
+__device__ __forceinline__ bool drop_keep(uint32_t w, int b, uint32_t t) {
+  return ((w >> (8 * b)) & 0xFFu) >= t;
+}
+
+}  // namespace fa

@@ -95,10 +95,17 @@ struct TileCopy {
   }
 
   // One tile (rows k0 .. k0 + BC - 1) of K (KEYS) or V (!KEYS) into Ts.
-  template <bool KEYS>
+  // UNI: pass the resource words through readfirstlane (all of them are
+  // wave-uniform, but in the dropout kernel the compiler loses track of that
+  // for some copies and would put the scalar operands in vector registers).
+  template <bool KEYS, bool UNI = false>
   __device__ __forceinline__ void issue(const uint16_t* Xh, uint16_t* Ts, int k0, int N, int w,
                                         int lane) const {
-    const i32x4 rs = make_rsrc_words(Xh + (int64_t)k0 * D, C::BC * D * 2);
+    i32x4 rs = make_rsrc_words(Xh + (int64_t)k0 * D, C::BC * D * 2);
+    if constexpr (UNI) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);
+    }
     if (k0 + C::BC <= N) {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t)
@@ -124,12 +131,14 @@ struct FwdSmem {
   uint16_t* v[3];
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 struct FwdWave {
   using C = FwdCfg<D>;
   static constexpr int BC = C::BC;
 
   FwdSmem sm;
+  DropArgs drop;  // dropout (DROP only)
+  int bh;
   const uint16_t* Kh;
   const uint16_t* Vh;
   int w, grp, lane, c32, g, N, qw0, qrow;
@@ -230,6 +239,26 @@ struct FwdWave {
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // Dropout bytes of this lane's keys 16 n + 8 g + 0..7 (chunk n): the
+    // lane computes the Philox call of 16-key group n = 2 m + g and swaps
+    // half of it with the other wave half, which computed group 2 m + 1 - g.
+    // After v_permlane32_swap(X = words 0-1, Y = words 2-3) both halves hold
+    // group 2 m's words in X and group 2 m + 1's in Y.
+    uint32_t rw[BC / 16][2];
+    if constexpr (DROP) {
+      const uint32_t jg0 = (uint32_t)(((t0 + t) * BC) >> 4);
+#pragma unroll
+      for (int m = 0; m < BC / 32; ++m) {
+        const u32x4 own = philox4x32_10(jg0 + 2 * m + g, (uint32_t)qrow, (uint32_t)bh,
+                                        drop.offset, drop.k0, drop.k1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(own[e], own[2 + e], false, false);
+          rw[2 * m][e] = r[0];
+          rw[2 * m + 1][e] = r[1];
+        }
+      }
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
@@ -238,6 +267,12 @@ struct FwdWave {
       for (int jj = 0; jj < 8; ++jj) {
         p[jj] = exp2_fast(fmaf(s[kc2 >> 1][(kc2 & 1) * 8 + jj], sl2, -m_use));
         rs += p[jj];
+      }
+      // the row sum takes every probability; the product with V only the kept ones
+      if constexpr (DROP) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          p[jj] = drop_keep(rw[kc2][jj >> 2], jj & 3, drop.t) ? p[jj] : 0.f;
       }
       pb[kc2] = pack8(p);
     }
@@ -261,14 +296,14 @@ struct FwdWave {
     if (GRP == 0) {
       matrix_phase<KB, VB>(t);
     } else {
-      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
       softmax_phase(t - 1);
     }
     block_barrier();
     if (GRP == 0) {
-      if (kn) cp.template issue<true>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
+      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
       softmax_phase(t);
     } else {
       matrix_phase<KB, VB>(t);
@@ -295,9 +330,11 @@ struct FwdWave {
 
 // SPLIT: workgroup = (head, query block, key range); writes the range's
 // unnormalised partials (see FwdArgs) instead of O and LSE.
-template <int D, bool CAUSAL, bool SPLIT>
+// DROP: dropout on the probabilities (a.drop); never combined with SPLIT.
+template <int D, bool CAUSAL, bool SPLIT, bool DROP = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(FwdArgs a) {
+  static_assert(!(SPLIT && DROP), "split-KV forward has no dropout");
   using C = FwdCfg<D>;
   constexpr int TILE = C::TILE;
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
@@ -321,8 +358,10 @@ fa_fwd_kernel(FwdArgs a) {
   if (CAUSAL) qb = nqb - 1 - qb;
 
   const int64_t hoff = (int64_t)bh * N * D;
-  FwdWave<D, CAUSAL> f;
+  FwdWave<D, CAUSAL, DROP> f;
   f.sm = FwdSmem{{k0s, k1s, k2s}, {v0s, v1s, v2s}};
+  f.drop = a.drop;
+  f.bh = bh;
   f.Kh = a.k + hoff;
   f.Vh = a.v + hoff;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -397,9 +436,9 @@ fa_fwd_kernel(FwdArgs a) {
     }
     return;
   }
-  // Epilogue: one division by l, LSE = (m + log2 l) ln 2.
+  // Epilogue: one division by l (and the dropout rescale), LSE = (m + log2 l) ln 2.
   if (f.qrow < N) {
-    const float inv = 1.f / l;
+    const float inv = DROP ? a.drop.scale / l : 1.f / l;
     uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -479,6 +518,23 @@ static hipError_t launch_fwd_splitkv_t(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 64) return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
   return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_dropout_t(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int64_t nqb = (a.N + C::BR - 1) / C::BR;
+  const int64_t grid = nqb * a.BH;
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false, true>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_dropout(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_fwd_dropout_t<64, true>(a, stream) : launch_fwd_dropout_t<64, false>(a, stream);
+  return causal ? launch_fwd_dropout_t<128, true>(a, stream)
+                : launch_fwd_dropout_t<128, false>(a, stream);
 }
 
 hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t stream) {

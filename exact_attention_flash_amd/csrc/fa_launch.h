@@ -8,6 +8,17 @@
 
 namespace fa {
 
+// Dropout on the attention probabilities (inactive unless a kernel is
+// instantiated for it).  Element (query i, key j) of head bh is kept iff byte
+// j mod 16 of Philox4x32-10(counter (j / 16, i, bh, offset), key (k0, k1)) is
+// >= t; kept values are multiplied by scale = 256 / (256 - t).
+struct DropArgs {
+  uint32_t t = 0;
+  float scale = 1.f;
+  uint32_t k0 = 0, k1 = 0;  // seed, low and high words
+  uint32_t offset = 0;
+};
+
 struct FwdArgs {
   const uint16_t* q;  // bf16 [B, H, N, d]
   const uint16_t* k;
@@ -28,6 +39,7 @@ struct FwdArgs {
   float* opart = nullptr;
   float* mpart = nullptr;
   float* lpart = nullptr;
+  DropArgs drop;
 };
 
 // FP8 forward: Q, K, V are OCP E4M3 codes, each tensor with one dequantisation
@@ -65,10 +77,14 @@ struct BwdArgs {
   int BH;
   float scale;        // softmax_scale, > 0
   float scale_log2;   // softmax_scale * log2(e)
+  DropArgs drop;
 };
 
 // Enqueue the forward kernel for head dim d (64 or 128).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Enqueue the forward kernel with dropout (a.drop) for head dim d.
+hipError_t launch_fwd_dropout(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // Enqueue the split-KV forward: the partial kernel over a.splits key ranges
 // per query block, then the merge kernel that writes O and LSE.
@@ -83,5 +99,9 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t s
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_kv(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_q(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+// The key-block and query-block passes with dropout (a.drop); the row pass is
+// the same with or without it.
+hipError_t launch_bwd_kv_dropout(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_q_dropout(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -69,7 +69,8 @@ enum fa_status {
   FA_ERR_ALIASING = 7,            /* an output overlaps an input or output */
   FA_ERR_HIP = 8,                 /* the HIP runtime rejected a launch */
   FA_ERR_BAD_SPLITS = 9,          /* num_splits outside 1..128 (split-KV forward) */
-  FA_ERR_BAD_DESCALE = 10         /* an FP8 descale factor is NaN, Inf or <= 0 */
+  FA_ERR_BAD_DESCALE = 10,        /* an FP8 descale factor is NaN, Inf or <= 0 */
+  FA_ERR_BAD_DROPOUT = 11         /* dropout_p is NaN, < 0 or rounds to 1 (see below) */
 };
 
 /*
@@ -156,6 +157,48 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
                        int causal, float softmax_scale,
                        float descale_q, float descale_k, float descale_v,
                        void* stream);
+
+/*
+ * Dropout on the attention probabilities.  "FlashAttention 的基本原理" (section
+ * 2.4) notes that the backward algorithm also covers dropout, and the apxml
+ * example applies it to the attention weights after the softmax.  With it,
+ *   O = (P o Z * s) V,   P = softmax(scale * Q K^T (masked)),
+ * where the keep mask Z is drawn, not passed: element (b, h, i, j) (query i,
+ * key j) is kept iff byte (j mod 16) of Philox4x32-10 (Salmon et al.,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with
+ *   counter = (floor(j / 16), i, b * H + h, offset),
+ *   key     = (seed mod 2^32, floor(seed / 2^32))
+ * (bytes numbered little-endian through the four output words) is >= t,
+ * t = floor(256 * dropout_p + 1/2), and s = 256 / (256 - t).  dropout_p must
+ * be >= 0 with t <= 255 (FA_ERR_BAD_DROPOUT otherwise); t = 0 keeps every
+ * element.  LSE is that of the scores (dropout does not change the softmax
+ * statistics).  The same (seed, offset) must be passed to the backward.
+ *   all other arguments : as flash_attn_fwd
+ * Deterministic.
+ */
+int flash_attn_fwd_dropout(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           int causal, float softmax_scale,
+                           float dropout_p, uint64_t seed, uint32_t offset,
+                           void* stream);
+
+/*
+ * Backward of flash_attn_fwd_dropout: dV = (P o Z s)^T dO, dP = (dO V^T) o Z s,
+ * dS = P o (dP - D) with D_i = sum_c dO_ic O_ic, dQ = scale dS K,
+ * dK = scale dS^T Q, the mask Z redrawn from the same (seed, offset).
+ *   o, lse : the outputs of flash_attn_fwd_dropout with the same arguments
+ *   all other arguments : as flash_attn_bwd and flash_attn_fwd_dropout
+ * Three launches (row pass, key-block pass, query-block pass).  Deterministic.
+ */
+int flash_attn_bwd_dropout(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           int causal, float softmax_scale,
+                           float dropout_p, uint64_t seed, uint32_t offset,
+                           void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape: two fp32

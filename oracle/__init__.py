@@ -59,6 +59,7 @@ from .dropout import (
     attention_forward_dropout,
     attention_forward_dropout_rows,
     attention_backward_dropout,
+    attention_backward_dropout_head,
 )
 from .online_softmax import (
     softmax_stats,
@@ -88,6 +89,7 @@ __all__ = [
     "attention_forward_dropout",
     "attention_forward_dropout_rows",
     "attention_backward_dropout",
+    "attention_backward_dropout_head",
     "softmax_stats",
     "merge_stats",
     "fold_blocks",

@@ -162,16 +162,23 @@ def attention_backward_dropout(q, k, v, dout, scale: float, causal: bool, p: flo
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, N, d = _heads(q, k, v)
-    s = dropout_scale(p)
-    sc_ = np.float64(scale)
     dQ, dK, dV = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
         for h in range(H):
-            P = softmax_rows(scores(q[b, h], k[b, h], scale, causal))[2]
-            Zs = dropout_mask(seed, offset, b * H + h, np.arange(N), N, p) * s
-            dV[b, h] = (P * Zs).T @ do[b, h]
-            dP = (do[b, h] @ v[b, h].T) * Zs
-            dS = softmax_row_grad(P, dP)
-            dQ[b, h] = sc_ * (dS @ k[b, h])
-            dK[b, h] = sc_ * (dS.T @ q[b, h])
+            dQ[b, h], dK[b, h], dV[b, h] = attention_backward_dropout_head(
+                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, p, seed, offset, b * H + h)
     return dQ, dK, dV
+
+
+def attention_backward_dropout_head(q, k, v, dout, scale: float, causal: bool, p: float,
+                                    seed: int, offset: int, bh: int):
+    """The gradients above for one head ``[N, d]`` whose head index is ``bh``."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    N = q.shape[0]
+    P = softmax_rows(scores(q, k, scale, causal))[2]
+    Zs = dropout_mask(seed, offset, bh, np.arange(N), N, p) * dropout_scale(p)
+    dV = (P * Zs).T @ do
+    dP = (do @ v.T) * Zs
+    dS = softmax_row_grad(P, dP)
+    sc_ = np.float64(scale)
+    return sc_ * (dS @ k), sc_ * (dS.T @ q), dV

@@ -19,7 +19,7 @@ from exact_attention_flash_amd.binding import LIB_PATH, load_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS, DESCALE = range(11)
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS, DESCALE, DROPOUT = range(12)
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                             reason="fake-pointer validation runs only without a GPU")
@@ -37,7 +37,8 @@ def test_library_exports_header_symbols():
                             "flash_attn_bwd_workspace_bytes", "flash_attn_status_string",
                             "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
                             "flash_attn_bwd_q_blocks", "flash_attn_fwd_splitkv",
-                            "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_fwd_fp8"])
+                            "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_fwd_fp8",
+                            "flash_attn_fwd_dropout", "flash_attn_bwd_dropout"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -48,7 +49,7 @@ def test_library_exports_header_symbols():
 
 def test_status_strings():
     lib = load_library()
-    for s in range(11):
+    for s in range(12):
         assert lib.flash_attn_status_string(s) not in (None, b"unknown status")
     assert lib.flash_attn_status_string(99) == b"unknown status"
 
@@ -160,6 +161,44 @@ def test_fwd_fp8_validation():
     assert _fwd_fp8(lib, lse=4 * A + 2 * n - 16) == ALIAS     # LSE inside O
 
 
+def _fwd_drop(lib, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=2, N=40, d=64, causal=1,
+              scale=0.125, p=0.1, seed=2**64 - 1, offset=2**32 - 1):
+    return lib.flash_attn_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, p, seed, offset,
+                                      None)
+
+
+def _bwd_drop(lib, ws_bytes=None, p=0.1, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+                ws=10 * A, B=1, H=2, N=16, d=128, causal=1, scale=0.1)
+    args.update(kw)
+    need = lib.flash_attn_bwd_workspace_bytes(args["B"], args["H"], args["N"], args["d"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return lib.flash_attn_bwd_dropout(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                      args["do"], args["dq"], args["dk"], args["dv"], args["ws"],
+                                      wsb, args["B"], args["H"], args["N"], args["d"],
+                                      args["causal"], args["scale"], p, 7, 0, None)
+
+
+@no_gpu
+def test_dropout_validation():
+    lib = load_library()
+    for bad in (-0.01, float("nan"), 1.0, 255.5 / 256, float("inf")):
+        assert _fwd_drop(lib, p=bad) == DROPOUT
+        assert _bwd_drop(lib, p=bad) == DROPOUT
+    assert _fwd_drop(lib, B=0, p=-1.0) == DROPOUT           # checked even when empty
+    assert _fwd_drop(lib, B=0, q=None) == FA_OK              # empty: no-op
+    assert _fwd_drop(lib, q=None) == NULLP
+    assert _fwd_drop(lib, d=80) == HEADDIM
+    assert _fwd_drop(lib, scale=-1.0) == SCALE
+    assert _fwd_drop(lib, o=A) == ALIAS
+    assert _bwd_drop(lib, ws_bytes=8) == WS
+    assert _bwd_drop(lib, dq=8 * A) == ALIAS
+    # largest allowed probability (t = 255), and p = 0
+    assert _fwd_drop(lib, p=255.4 / 256) == HIPERR
+    assert _fwd_drop(lib, p=0.0) == HIPERR
+    assert _bwd_drop(lib, p=0.0) == HIPERR
+
+
 def _bwd(lib, ws_bytes=None, **kw):
     args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
                 ws=10 * A, B=1, H=2, N=16, d=128, causal=1, scale=0.1)
@@ -221,6 +260,8 @@ def test_valid_call_without_device_reports_hip_error():
     assert _fwd(lib) == HIPERR
     assert _fwd_split(lib) == HIPERR
     assert _fwd_fp8(lib) == HIPERR
+    assert _fwd_drop(lib) == HIPERR
+    assert _bwd_drop(lib) == HIPERR
 
 
 def test_python_binding_rejects_cpu_tensors():
