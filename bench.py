@@ -41,8 +41,10 @@ KERNEL_SOURCES = ["fa_common.h", "fa_launch.h", "fa_fwd.hip", "fa_fwd_fp8.hip", 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 untimed steps (about 0.15 s): shorter warmups measure the GPU
+    # before its clock has settled and read about 5% low
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c5", help="named workload (default c5: fwd+bwd)")
     ap.add_argument("--cpu-heads", type=int, default=40,
                     help="heads of the step the CPU oracle times (0 = skip cpu_baseline)")
@@ -50,6 +52,9 @@ def parse_args():
                     help="also time the forward on small-grid shapes (c2's, and few heads with "
                          "long sequences) plain and split-KV with this many key ranges "
                          "(0 = skip); reported under 'splitkv'")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="also time the fwd+bwd step with dropout of this probability next to\n"
+                         "the plain step (0 = skip); reported under 'dropout'")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the FP8 (E4M3) forward next to the bf16 forward on the\n"
                          "fwd+bwd and long-context shapes; reported under 'fp8_forward'")
@@ -202,6 +207,52 @@ def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
     return out
 
 
+def dropout_measure(fa, tensors, wl, causal: bool, p: float, iters: int = 10) -> dict:
+    """The fwd+bwd step with dropout (probability p) next to the plain one on
+    the bench workload, timed with HIP events on the current stream."""
+    import torch
+    q, k, v, do, o, lse, dq, dk, dv, ws = tensors
+    scale = wl.scale
+    stream = torch.cuda.current_stream()
+    seed = 0x5EED
+
+    def run(drop: bool, evs=None):
+        if evs:
+            evs[0].record(stream)
+        if drop:
+            fa.flash_attn_fwd_dropout(q, k, v, p, seed, 0, causal=causal, softmax_scale=scale,
+                                      out=o, lse=lse)
+        else:
+            fa.flash_attn_fwd(q, k, v, causal=causal, softmax_scale=scale, out=o, lse=lse)
+        if evs:
+            evs[1].record(stream)
+        if drop:
+            fa.flash_attn_bwd_dropout(do, q, k, v, o, lse, p, seed, 0, causal=causal,
+                                      softmax_scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            fa.flash_attn_bwd(do, q, k, v, o, lse, causal=causal, softmax_scale=scale, dq=dq,
+                              dk=dk, dv=dv, workspace=ws)
+        if evs:
+            evs[2].record(stream)
+
+    out = {"p": p}
+    f_fwd, f_bwd = wl.flops_fwd(causal), wl.flops_bwd(causal)
+    for name, drop in (("plain", False), ("dropout", True)):
+        for _ in range(3):
+            run(drop)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+        torch.cuda.synchronize()
+        for e in evs:
+            run(drop, e)
+        torch.cuda.synchronize()
+        fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / iters
+        bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / iters
+        out[name] = {"fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+                     "fwd_tflops": round(f_fwd / fwd / 1e9, 2),
+                     "fwd_bwd_tflops": round((f_fwd + f_bwd) / (fwd + bwd) / 1e9, 2)}
+    return out
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -337,6 +388,9 @@ def main() -> int:
     }
     if args.splitkv > 0:
         line["splitkv"] = splitkv_measure(fa, make_inputs, args.splitkv)
+    if args.dropout > 0:
+        line["dropout"] = dropout_measure(fa, (q, k, v, do, o, lse, dq, dk, dv, ws), wl, causal,
+                                          args.dropout)
     if args.fp8:
         from exact_attention_flash_amd.inputs import make_inputs_fp8
         line["fp8_forward"] = fp8_measure(fa, make_inputs, make_inputs_fp8)
