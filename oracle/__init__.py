@@ -49,6 +49,10 @@ from .fp8 import (
     dequantize,
     attention_forward_fp8,
     attention_forward_fp8_rows,
+    hadamard_matrix,
+    incoherent_rotation,
+    encode_e4m3,
+    quantize_e4m3,
 )
 from .dropout import (
     philox,
@@ -81,6 +85,10 @@ __all__ = [
     "dequantize",
     "attention_forward_fp8",
     "attention_forward_fp8_rows",
+    "hadamard_matrix",
+    "incoherent_rotation",
+    "encode_e4m3",
+    "quantize_e4m3",
     "philox",
     "dropout_threshold",
     "dropout_scale",

@@ -78,3 +78,60 @@ def attention_forward_fp8_rows(q8, k8, v8, descale_q: float, descale_k: float,
     return attention_forward_rows(dequantize(q8, descale_q),
                                   dequantize(k8, descale_k),
                                   dequantize(v8, descale_v), scale, causal, rows)
+
+
+# ------------------------------------------------------- incoherent processing
+# "FlashAttention 系列技术详解", FlashAttention-3 section: before quantising,
+# multiply the queries and keys by a random orthogonal matrix, a Hadamard
+# transform, which spreads large entries over all coordinates and so lowers
+# the quantisation error, at O(d log d) per row.  Reading: the matrix is
+# M = diag(signs) H_d / sqrt(d), with H_d the Sylvester Hadamard matrix and
+# random signs passed in; (Q M)(K M)^T = Q K^T because M M^T = I, and V is
+# not transformed.
+
+def hadamard_matrix(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix: H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    H = np.ones((1, 1))
+    while H.shape[0] < d:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def incoherent_rotation(x, signs) -> np.ndarray:
+    """x M for M = diag(signs) H_d / sqrt(d), over the last axis, float64."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.asarray(signs, dtype=np.float64)
+    d = x.shape[-1]
+    return (x * s) @ hadamard_matrix(d) / np.sqrt(d)
+
+
+_E4M3_POS = None
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """Nearest E4M3 code to each value (ties to the even code), saturating at
+    +-448; finite inputs only.  Written as a nearest-neighbour search over the
+    decoded finite codes, the definition of round-to-nearest-even."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = decode_e4m3(np.arange(0x7F, dtype=np.uint8))  # codes 0 .. 0x7E, increasing
+    v = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(v), _E4M3_POS[-1])
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def quantize_e4m3(x, signs=None):
+    """Codes and descale of a tensor (rows over the last axis), optionally
+    rotated first: y = x M (or x), descale = float32(amax|y| / 448),
+    codes = e4m3(y / descale)."""
+    y = np.asarray(x, dtype=np.float64) if signs is None else incoherent_rotation(x, signs)
+    amax = float(np.max(np.abs(y))) if y.size else 0.0
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    return encode_e4m3(y / descale), descale

@@ -108,3 +108,71 @@ def test_rows_variant_matches_whole_head():
                                                0.25, True, rows)
     np.testing.assert_allclose(Or, O[0, 0, rows], rtol=1e-13)
     np.testing.assert_allclose(Lr, L[0, 0, rows], rtol=1e-13)
+
+
+# ---------------------------------------------------------------- incoherent processing
+import scipy.linalg
+
+
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128])
+def test_hadamard_matches_scipy(d):
+    assert np.array_equal(of8.hadamard_matrix(d), scipy.linalg.hadamard(d))
+
+
+def test_rotation_is_orthogonal_and_keeps_scores():
+    rng = np.random.default_rng(3)
+    for d in (64, 128):
+        signs = rng.choice([-1.0, 1.0], d)
+        M = of8.incoherent_rotation(np.eye(d), signs)
+        np.testing.assert_allclose(M @ M.T, np.eye(d), atol=1e-14)
+        q, k = rng.standard_normal((50, d)), rng.standard_normal((40, d))
+        qr, kr = of8.incoherent_rotation(q, signs), of8.incoherent_rotation(k, signs)
+        np.testing.assert_allclose(qr @ kr.T, q @ k.T, rtol=1e-12, atol=1e-12)
+    # spreads a spike: a unit vector becomes +-1/sqrt(d) everywhere
+    e = np.zeros(64)
+    e[5] = 1.0
+    np.testing.assert_allclose(np.abs(of8.incoherent_rotation(e, np.ones(64))), 1 / 8)
+
+
+def test_encoder_matches_torch():
+    vals = _torch_decode(ALL_CODES)
+    fin = np.unique(vals[np.isfinite(vals)])
+    mids = (fin[1:] + fin[:-1]) / 2
+    rng = np.random.default_rng(4)
+    x = np.concatenate([fin, mids, -mids, rng.standard_normal(5000) * 30,
+                        rng.standard_normal(5000) * 1e-3])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(of8.encode_e4m3(x), ref)
+    assert of8.encode_e4m3(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]   # saturates
+
+
+def test_quantize_roundtrip():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((300, 64))
+    for signs in (None, rng.choice([-1.0, 1.0], 64)):
+        codes, ds = of8.quantize_e4m3(x, signs)
+        y = x if signs is None else of8.incoherent_rotation(x, signs)
+        back = of8.decode_e4m3(codes) * ds
+        assert np.max(np.abs(of8.decode_e4m3(codes))) == 448.0          # amax at the top
+        normal = np.abs(y / ds) >= 2 ** -6
+        assert np.max(np.abs(back - y)[normal] / np.abs(y)[normal]) <= 2 ** -4 * (1 + 1e-6)
+
+
+def test_rotation_lowers_quantisation_error_with_outliers():
+    """The pages' claim, on the oracle: with a few large channels in Q and K,
+    quantising after the rotation gives a much smaller score error."""
+    rng = np.random.default_rng(6)
+    d, N = 128, 256
+    q, k = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    q[:, :4] *= 30
+    k[:, :4] *= 30
+    ref = q @ k.T
+    signs = rng.choice([-1.0, 1.0], d)
+    err = {}
+    for name, s in (("plain", None), ("rotated", signs)):
+        cq, dq = of8.quantize_e4m3(q, s)
+        ck, dk = of8.quantize_e4m3(k, s)
+        sc = (of8.decode_e4m3(cq) * dq) @ (of8.decode_e4m3(ck) * dk).T
+        err[name] = np.sqrt(np.mean((sc - ref) ** 2))
+    assert err["rotated"] < 0.5 * err["plain"], err

@@ -312,3 +312,59 @@ def test_dropout_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
         monkeypatch.setattr(oracle, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ---------------------------------------------------------------- incoherent processing
+def _hadamard_other_sylvester(d):
+    H = np.ones((1, 1))
+    while H.shape[0] < d:
+        H = np.block([[H, H], [-H, H]])
+    return H
+
+
+def _rotation_unnormalised(x, signs):
+    return (np.asarray(x, dtype=np.float64) * np.asarray(signs, dtype=np.float64)) @ \
+        of8.hadamard_matrix(np.asarray(x).shape[-1])
+
+
+def _encode_ties_to_odd(x):
+    pos = of8.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    v = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(v), pos[-1])
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, len(pos) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - pos[lo], pos[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 1))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def _pin_hadamard_scipy():
+    from tests.test_oracle_fp8 import test_hadamard_matches_scipy
+    test_hadamard_matches_scipy(8)
+
+
+def _pin_rotation():
+    from tests.test_oracle_fp8 import test_rotation_is_orthogonal_and_keeps_scores
+    test_rotation_is_orthogonal_and_keeps_scores()
+
+
+def _pin_encoder():
+    from tests.test_oracle_fp8 import test_encoder_matches_torch
+    test_encoder_matches_torch()
+
+
+MUTATIONS_ROT = [
+    ("hadamard_matrix", _hadamard_other_sylvester, _pin_hadamard_scipy),
+    ("incoherent_rotation", _rotation_unnormalised, _pin_rotation),
+    ("encode_e4m3", _encode_ties_to_odd, _pin_encoder),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", MUTATIONS_ROT,
+                         ids=[m[1].__name__ for m in MUTATIONS_ROT])
+def test_rotation_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
+    pin()
+    monkeypatch.setattr(of8, target, bad)
+    with pytest.raises(AssertionError):
+        pin()
