@@ -75,6 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                ctypes.c_size_t, i64, i64, i64, i64, ci, fl,
                                                fl, u64, u32, vp]
         lib.flash_attn_bwd_dropout.restype = ci
+        lib.flash_attn_quantize_fp8.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, vp, vp]
+        lib.flash_attn_quantize_fp8.restype = ci
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -177,6 +179,39 @@ def flash_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                     _stream_ptr(q.device, stream))
     _check(st)
     return out, lse
+
+
+def flash_attn_quantize_fp8(x: torch.Tensor, signs: torch.Tensor | None = None,
+                            codes: torch.Tensor | None = None, descale: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None):
+    """E4M3 codes of a bf16 tensor (rows over the last dim, d = 64 or 128),
+    rotated by diag(signs) H_d / sqrt(d) first when ``signs`` is given.
+    Returns ``(codes, descale)``: uint8 codes of x's shape and a float32
+    device tensor [1] holding amax / 448."""
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a bfloat16 tensor")
+    if x.device.type != "cuda" or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous GPU tensor")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if signs is not None and (signs.dtype != torch.float32 or signs.shape != (d,)
+                              or signs.device != x.device or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 [d] tensor on x's device")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    if codes.dtype not in FP8_DTYPES or codes.shape != x.shape or not codes.is_contiguous() \
+            or codes.device != x.device:
+        raise ValueError("codes must be a contiguous one-byte tensor of x's shape on x's device")
+    descale = torch.empty(1, dtype=torch.float32, device=x.device) if descale is None else descale
+    workspace = torch.empty(1, dtype=torch.int32, device=x.device) if workspace is None else workspace
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.flash_attn_quantize_fp8(x.data_ptr(), codes.data_ptr(), descale.data_ptr(),
+                                         workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), rows, d,
+                                         None if signs is None else signs.data_ptr(),
+                                         _stream_ptr(x.device, stream))
+    _check(st)
+    return codes, descale
 
 
 def flash_attn_fwd_splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:

@@ -21,7 +21,7 @@ LIB_NAME = "libexact_attention_flash_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip"]
+SOURCES = ["api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_quant.hip", "fa_bwd.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -56,6 +56,17 @@ struct Fp8FwdArgs {
   float descale_v;    // > 0
 };
 
+// FP8 quantisation of a bf16 tensor of `rows` rows of d values, optionally
+// rotated by diag(signs) H_d / sqrt(d) first.
+struct QuantArgs {
+  const uint16_t* x;   // bf16 [rows, d]
+  uint8_t* codes;      // E4M3 [rows, d]
+  float* descale;      // out: amax / 448 (1 float)
+  uint32_t* amax;      // workspace: fp32 bits of the running amax
+  const float* signs;  // [d] of +-1, or nullptr (no rotation)
+  int64_t rows;
+};
+
 // Query rows per block of the backward key-block pass; the row vectors in
 // the backward workspace are padded to a multiple of it.
 constexpr int kBwdQueryBlock = 64;
@@ -92,6 +103,9 @@ hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t 
 
 // Enqueue the FP8 forward kernel for head dim d (64 or 128).
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Enqueue the FP8 quantisation (three launches) for head dim d (64 or 128).
+hipError_t launch_quant_fp8(const QuantArgs& a, int d, hipStream_t stream);
 
 // The three backward stages, each one kernel launch, for head dim d (64 or
 // 128): the row pass, the pass over key blocks (dK, dV) and the pass over

@@ -159,6 +159,28 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
                        void* stream);
 
 /*
+ * FP8 quantisation for flash_attn_fwd_fp8, with optional incoherent
+ * processing ("FlashAttention 系列技术详解", FlashAttention-3 section: the
+ * queries and keys are multiplied by a random orthogonal matrix, a Hadamard
+ * transform, to spread large entries and lower the quantisation error).
+ *   x         : in,  bf16 [rows, d] (e.g. Q or K as [B*H*N, d])
+ *   codes     : out, E4M3 [rows, d]: codes of y / descale, nearest even
+ *   descale   : out, device fp32 scalar: amax|y| / 448 (1 if y is all zero)
+ *   workspace : device memory of at least 4 bytes, 4-byte aligned, no init
+ *   signs     : device fp32 [d] of +1 / -1, or NULL.  With signs,
+ *               y = x M, M = diag(signs) H_d / sqrt(d) (H_d the Sylvester
+ *               Hadamard matrix); apply the same signs to Q and K (then
+ *               Q M (K M)^T = Q K^T) and pass V with NULL.  Without, y = x.
+ *   d         : 64 or 128
+ * x needs 16-byte alignment, codes 16 bytes, descale and signs 4 bytes;
+ * codes, descale and workspace must not overlap x, signs or each other.
+ * rows = 0 is a no-op.  Three launches on `stream`.  Deterministic.
+ */
+int flash_attn_quantize_fp8(const void* x, void* codes, float* descale,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t rows, int64_t d, const float* signs, void* stream);
+
+/*
  * Dropout on the attention probabilities.  "FlashAttention 的基本原理" (section
  * 2.4) notes that the backward algorithm also covers dropout, and the apxml
  * example applies it to the attention weights after the softmax.  With it,

@@ -38,7 +38,8 @@ def test_library_exports_header_symbols():
                             "flash_attn_bwd_preprocess", "flash_attn_bwd_kv_blocks",
                             "flash_attn_bwd_q_blocks", "flash_attn_fwd_splitkv",
                             "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_fwd_fp8",
-                            "flash_attn_fwd_dropout", "flash_attn_bwd_dropout"])
+                            "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
+                            "flash_attn_quantize_fp8"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -197,6 +198,26 @@ def test_dropout_validation():
     assert _fwd_drop(lib, p=255.4 / 256) == HIPERR
     assert _fwd_drop(lib, p=0.0) == HIPERR
     assert _bwd_drop(lib, p=0.0) == HIPERR
+
+
+def _quant(lib, x=A, codes=2 * A, ds=3 * A, ws=4 * A, wsb=4, rows=100, d=128, signs=5 * A):
+    return lib.flash_attn_quantize_fp8(x, codes, ds, ws, wsb, rows, d, signs, None)
+
+
+@no_gpu
+def test_quantize_validation():
+    lib = load_library()
+    assert _quant(lib, rows=0, x=None) == FA_OK
+    assert _quant(lib, rows=-1) == SHAPE
+    assert _quant(lib, d=96) == HEADDIM
+    assert _quant(lib, x=None) == NULLP and _quant(lib, ws=None) == NULLP
+    assert _quant(lib, x=A + 8) == MISAL and _quant(lib, signs=5 * A + 2) == MISAL
+    assert _quant(lib, wsb=2) == WS
+    assert _quant(lib, codes=A + 16) == ALIAS                  # codes inside x
+    assert _quant(lib, ws=3 * A) == ALIAS                      # workspace on descale
+    assert _quant(lib, ds=5 * A) == ALIAS                      # descale on signs
+    assert _quant(lib, signs=None) == HIPERR                   # no rotation is allowed
+    assert _quant(lib) == HIPERR
 
 
 def _bwd(lib, ws_bytes=None, **kw):

@@ -175,3 +175,76 @@ def test_fwd_fp8_full_size_sampled(name, B, H, N, d, causal, seed):
         og = bf16_to_f64(o[b, h][torch.as_tensor(rows, device=o.device)])
         check_o_fp8(og, O_ref, a_abs, floor, sig2, f"O (fp8) head {b},{h}")
         check_lse(lse[b, h].cpu().numpy()[rows].astype(np.float64), L_ref)
+
+
+# ------------------------------------------------- quantisation and incoherent processing
+from exact_attention_flash_amd import flash_attn_quantize_fp8
+from exact_attention_flash_amd.inputs import f32_to_bf16_bits, make_inputs
+
+from gpu_util import bf16_to_f64 as _bf, to_device as _dev
+
+_E4M3_VALS = np.sort(np.unique(np.abs(oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8)))))
+
+
+def _step_distance(c1, c2):
+    """Distance between codes in units of representable steps (same sign)."""
+    v1, v2 = oracle.decode_e4m3(c1), oracle.decode_e4m3(c2)
+    i1 = np.searchsorted(_E4M3_VALS, np.abs(v1)) * np.sign(v1)
+    i2 = np.searchsorted(_E4M3_VALS, np.abs(v2)) * np.sign(v2)
+    return np.abs(i1 - i2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantize_parity(d, rotate):
+    _say(f"fp8 quantize d={d} rotate={rotate}")
+    x = make_inputs(2, 3, 150, d, seed=60 + d + rotate)["q"]
+    xt = _dev(x)
+    rng = np.random.default_rng(d)
+    signs = rng.choice([-1.0, 1.0], d).astype(np.float32) if rotate else None
+    codes, ds = flash_attn_quantize_fp8(xt, None if signs is None else torch.from_numpy(signs).cuda())
+    torch.cuda.synchronize()
+    cg = codes.cpu().numpy()
+    dsg = float(ds.item())
+    xf = oracle.widen_bf16(x)
+    ref_codes, ref_ds = oracle.quantize_e4m3(xf, signs)
+    if not rotate:
+        assert dsg == ref_ds                  # exact amax, correctly rounded division
+    else:
+        assert abs(dsg - ref_ds) <= 1e-6 * ref_ds
+    # the codes of the oracle's y under the GPU's descale
+    y = xf if signs is None else oracle.incoherent_rotation(xf, signs)
+    expect = oracle.encode_e4m3(y / dsg)
+    dist = _step_distance(cg, expect)
+    assert dist.max() <= 1, f"codes off by {dist.max()} steps"
+    assert (cg == expect).mean() >= (1.0 if not rotate else 0.999), (cg == expect).mean()
+    assert int(np.max(np.abs(oracle.decode_e4m3(cg)))) == 448
+
+
+def test_incoherent_processing_lowers_fp8_error():
+    """The pages' claim end to end on the GPU: with four large channels in Q
+    and K, FP8 attention over rotated-then-quantised Q and K is closer to the
+    exact bf16-input attention than over plainly quantised ones."""
+    B, H, N, d = 1, 4, 512, 128
+    x = make_inputs(B, H, N, d, seed=77)
+    for n in ("q", "k"):
+        v = oracle.widen_bf16(x[n]).astype(np.float32)
+        v[..., :4] *= 32.0                     # a power of two: still exact in bf16
+        x[n] = f32_to_bf16_bits(v)
+    scale = default_scale(d)
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, False)
+    signs = torch.from_numpy(np.random.default_rng(1).choice([-1.0, 1.0], d).astype(np.float32)).cuda()
+    q, k, v = (_dev(x[n]) for n in ("q", "k", "v"))
+    v8, dv = flash_attn_quantize_fp8(v)
+    err = {}
+    for name, sg in (("plain", None), ("rotated", signs)):
+        q8, dq = flash_attn_quantize_fp8(q, sg)
+        k8, dk = flash_attn_quantize_fp8(k, sg)
+        o, lse = flash_attn_fwd_fp8(q8, k8, v8, dq.item(), dk.item(), dv.item(), softmax_scale=scale)
+        torch.cuda.synchronize()
+        err[name] = (float(np.sqrt(np.mean((_bf(o) - O_ref) ** 2))),
+                     float(np.max(np.abs(lse.cpu().numpy() - L_ref))))
+    _say(f"  O rms error plain {err['plain'][0]:.3e} rotated {err['rotated'][0]:.3e}; "
+         f"LSE max error plain {err['plain'][1]:.3e} rotated {err['rotated'][1]:.3e}")
+    assert err["rotated"][0] < 0.6 * err["plain"][0]
+    assert err["rotated"][1] < 0.6 * err["plain"][1]
