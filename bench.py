@@ -199,7 +199,20 @@ def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
                                                x8["descale_v"], causal=causal, out=o, lse=lse))
         t16 = avg(lambda: fa.flash_attn_fwd(q, k, v, causal=causal, out=o, lse=lse))
         f = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        # quantising Q with incoherent processing (rotation by a random-sign
+        # Hadamard matrix): two passes over the bf16 input, one write of the
+        # codes, 5 bytes per element of algorithmic traffic
+        signs = torch.from_numpy(np.random.default_rng(seed).choice([-1.0, 1.0], d)
+                                 .astype(np.float32)).cuda()
+        codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+        dsc = torch.empty(1, dtype=torch.float32, device=q.device)
+        wsq = torch.empty(1, dtype=torch.int32, device=q.device)
+        tq = avg(lambda: fa.flash_attn_quantize_fp8(q, signs, codes=codes, descale=dsc,
+                                                    workspace=wsq))
+        qbytes = 5.0 * q.numel()
         out.append({"shape": f"{'causal' if causal else 'full'} fwd B={B} H={H} N={N} d={d}",
+                    "quantize_rotated_ms": round(tq, 4),
+                    "quantize_rotated_gbs": round(qbytes / tq / 1e6, 1),
                     "fp8_ms": round(t8, 4), "fp8_tflops": round(f / t8 / 1e9, 2),
                     "fp8_frac_of_fp8_peak": round(f / t8 / 1e9 / PEAK_FP8_TFLOPS, 4),
                     "bf16_ms": round(t16, 4), "bf16_tflops": round(f / t16 / 1e9, 2),

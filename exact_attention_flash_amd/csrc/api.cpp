@@ -390,7 +390,7 @@ int flash_attn_quantize_fp8(const void* x, void* codes, float* descale, void* wo
   if ((rows + 15) / 16 > INT32_MAX) return FA_ERR_BAD_SHAPE;
   if (!x || !codes || !descale || !workspace) return FA_ERR_NULL_POINTER;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(descale, 4) || !aligned(workspace, 4) ||
-      (signs && !aligned(signs, 4)))
+      (signs && !aligned(signs, 16)))
     return FA_ERR_MISALIGNED;
   if (workspace_bytes < 4) return FA_ERR_WORKSPACE_TOO_SMALL;
   const size_t n = size_t(rows) * size_t(d);

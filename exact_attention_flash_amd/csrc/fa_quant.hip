@@ -11,16 +11,18 @@
 //
 // Per tensor: y = x M (or y = x), descale = amax|y| / 448 (fp32),
 // codes = E4M3(y / descale), round to nearest even (of the exact quotient,
-// not of its fp32 rounding: see e4m3_ready_quotient).  Three launches: clear
+// not of an fp32 rounding of it: see e4m3_ready_quotient).  Three launches: clear
 // the amax word, reduce amax|y| (atomic max on the fp32 bits, which order
 // like the values for y >= 0), then recompute y and write the codes; block
-// 0 of the last launch writes the descale.
+// 0 of the last launch writes the descale.  The amax pass strides over the
+// rows with a bounded grid and issues one atomic per workgroup.
 //
-// Layout: a row of d bf16 values is handled by d / 8 consecutive lanes, 8
-// values (16 bytes) each.  The fast Walsh-Hadamard transform runs its first
-// three butterfly levels inside a lane and the rest across lanes with XOR
-// shuffles (lane distance 1, 2, 4, 8).  Memory-bound: 2 bytes read per
-// element in each of the two passes, 1 byte written.
+// Layout: a row of d bf16 values is handled by 4 consecutive lanes, d / 4
+// values each (contiguous, so a wave reads 16 whole rows).  The fast
+// Walsh-Hadamard transform runs all but its two top butterfly levels inside
+// a lane and those two with XOR shuffles inside a quad (lane distance 1, 2).
+// Memory-bound: 2 bytes read per element in each of the two passes, 1 byte
+// written.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -28,116 +30,169 @@ namespace fa {
 
 template <int D>
 struct QuantCfg {
-  static constexpr int L = D / 8;          // lanes per row
+  static constexpr int L = 4;              // lanes per row
+  static constexpr int E = D / L;          // values per lane
   static constexpr int NT = 256;           // threads per workgroup
   static constexpr int RPB = NT / L;       // rows per workgroup
 };
 
-// y for the 8 values of lane position lr (0 .. D/8 - 1) of a row.  Every
-// lane of the wave must call it (the shuffles are wave-wide); lanes without a
-// row pass zeros.
+// The value of lane (lane ^ m) for m = 1 or 2: a DPP quad permutation
+// (quad_perm [1,0,3,2] or [2,3,0,1]), a plain VALU move.
+__device__ __forceinline__ float quad_xor(float x, int m) {
+  const int r = m == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)
+                       : __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false);
+  return __int_as_float(r);
+}
+
+// y for the E values of lane position lr (0 .. 3) of a row.  Every lane of
+// the wave must call it (the shuffles are wave-wide); lanes without a row
+// pass zeros.
 template <int D>
-__device__ __forceinline__ void load_rotate(const QuantArgs& a, int64_t row, int lr, float v[8]) {
-  constexpr int L = D / 8;
+__device__ __forceinline__ void load_rotate(const QuantArgs& a, int64_t row, int lr,
+                                            float v[QuantCfg<D>::E]) {
+  constexpr int E = QuantCfg<D>::E;
   if (row < a.rows) {
-    const u32x4 w = load_global<u32x4>(a.x + row * D + 8 * lr);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = bf16_to_f32((uint16_t)(w[j] & 0xffffu));
-      v[2 * j + 1] = bf16_to_f32((uint16_t)(w[j] >> 16));
+    for (int c = 0; c < E / 8; ++c) {
+      const u32x4 w = load_global<u32x4>(a.x + row * D + E * lr + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * c + 2 * j] = bf16_to_f32((uint16_t)(w[j] & 0xffffu));
+        v[8 * c + 2 * j + 1] = bf16_to_f32((uint16_t)(w[j] >> 16));
+      }
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int e = 0; e < E; ++e) v[e] = 0.f;
   }
   if (a.signs == nullptr) return;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] *= a.signs[8 * lr + e];
-  // butterflies over index bits 0..2 (inside the lane)
+  for (int c = 0; c < E / 4; ++c) {
+    const f32x4 sg = load_global<f32x4>(a.signs + E * lr + 4 * c);
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
+    for (int e = 0; e < 4; ++e) v[4 * c + e] *= sg[e];
+  }
+  // butterflies over the index bits inside the lane
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+  for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
       if ((e & h) == 0) {
         const float x0 = v[e], x1 = v[e + h];
         v[e] = x0 + x1;
         v[e + h] = x0 - x1;
       }
-  // bits 3.. log2(D) - 1: the partner lane holds the other half of each pair;
-  // the lane with the bit clear keeps the sum, the other the difference
+  // the two top index bits are the lane position: the partner lane (xor 1,
+  // then xor 2, inside a quad) holds the other half of each pair; the lane
+  // with the bit clear keeps the sum, the other the difference
 #pragma unroll
-  for (int m = 1; m < L; m <<= 1) {
+  for (int m = 1; m < 4; m <<= 1) {
     const bool upper = (lr & m) != 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __shfl_xor(v[e], m, 64);
+    for (int e = 0; e < E; ++e) {
+      const float p = quad_xor(v[e], m);
       v[e] = upper ? p - v[e] : v[e] + p;
     }
   }
   constexpr float kInvSqrtD = D == 128 ? 0.08838834764831845f : 0.125f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] *= kInvSqrtD;
+  for (int e = 0; e < E; ++e) v[e] *= kInvSqrtD;
 }
 
 // The E4M3 rounding (nearest even) of the exact quotient v / ds, returned as
-// an fp32 value whose own nearest-even E4M3 rounding is that code.  q = v / ds
-// rounded to fp32 lands on the same side of every E4M3 midpoint as the exact
-// quotient, or on the midpoint itself; in that case the remainder
-// v - q ds (exact through the FMA) tells on which side the quotient lies, and
-// q moves one ulp that way so that the conversion does not see a tie.
-__device__ __forceinline__ float e4m3_ready_quotient(float v, float ds) {
-  float q = v / ds;
-  const float r = fmaf(-q, ds, v);
+// an fp32 value whose own nearest-even E4M3 rounding is that code.
+// q = v * inv (inv = 1 / ds rounded) is within two ulps of the quotient, so
+// unless q lies within a few ulps of an E4M3 midpoint it is on the same side
+// of every midpoint as the quotient and converts to the right code.  Near a
+// midpoint the sign of v - mid * ds (exact through the FMA) tells on which
+// side the quotient lies (or that it is the midpoint), and q is set one ulp
+// that way from the midpoint (or to it, a true tie).  Below the normal E4M3
+// range (|q| < 2^-6, midpoints at odd multiples of 2^-10) the same test runs
+// on the correctly rounded division.
+__device__ __forceinline__ float e4m3_ready_quotient(float v, float ds, float inv) {
+  float q = v * inv;
   const uint32_t b = __float_as_uint(q);
   const uint32_t mag = b & 0x7fffffffu;
-  bool mid;
-  if (mag >= 0x3c800000u) {          // |q| >= 2^-6: normal E4M3 range
-    mid = (mag & 0xfffffu) == 0x80000u;  // the mantissa bits below E4M3's three are 100..0
-  } else {                           // subnormal range: midpoints are odd multiples of 2^-10
-    const float t = fabsf(q) * 1024.f;
-    mid = t == rintf(t) && (((int)t) & 1);
+  // normal range, branch-free: mantissa bits below E4M3's top three read
+  // 100..0 at a midpoint
+  const float mid = __uint_as_float((b & 0xfff00000u) | 0x80000u);
+  const float r = fmaf(-mid, ds, v);
+  const uint32_t mb = __float_as_uint(mid);
+  const float qm = r == 0.f ? mid : __uint_as_float((r > 0.f) == (mid > 0.f) ? mb + 1u : mb - 1u);
+  q = (mag & 0xfffffu) - 0x7fffcu <= 8u ? qm : q;
+  const bool sub = mag < 0x3c800000u;
+  if (__builtin_amdgcn_ballot_w64(sub)) {  // wave-uniform; rare for amax-scaled data
+    if (sub) {
+      q = v / ds;
+      const float rr = fmaf(-q, ds, v);
+      const uint32_t bq = __float_as_uint(q);
+      const float t = fabsf(q) * 1024.f;
+      if (t == rintf(t) && (((int)t) & 1) && rr != 0.f)
+        q = __uint_as_float((rr > 0.f) == (q > 0.f) ? bq + 1u : bq - 1u);
+    }
   }
-  if (mid && r != 0.f) q = __uint_as_float((r > 0.f) == (q > 0.f) ? b + 1u : b - 1u);
   return q;
 }
 
 __global__ void fa_quant_clear_kernel(QuantArgs a) { *a.amax = 0u; }
 
+// Grid-stride over row blocks (the stride is uniform per workgroup, so every
+// wave runs the same iterations and reaches every shuffle), then one atomic
+// per workgroup: atomics on one address serialise in L2.
 template <int D>
 __global__ void __launch_bounds__(256) fa_quant_amax_kernel(QuantArgs a) {
   using C = QuantCfg<D>;
-  const int64_t row = (int64_t)blockIdx.x * C::RPB + threadIdx.x / C::L;
+  __shared__ float wmax[C::NT / 64];
   const int lr = threadIdx.x % C::L;
-  float v[8];
-  load_rotate<D>(a, row, lr, v);
   float m = 0.f;
+  for (int64_t r0 = (int64_t)blockIdx.x * C::RPB; r0 < a.rows; r0 += (int64_t)gridDim.x * C::RPB) {
+    float v[C::E];
+    load_rotate<D>(a, r0 + threadIdx.x / C::L, lr, v);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    for (int e = 0; e < C::E; ++e) m = fmaxf(m, fabsf(v[e]));
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(a.amax, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wmax[0];
+#pragma unroll
+    for (int i = 1; i < C::NT / 64; ++i) b = fmaxf(b, wmax[i]);
+    atomicMax(a.amax, __float_as_uint(b));
+  }
 }
+
+// Workgroups of the amax pass: enough to fill the chip several times over.
+constexpr int64_t kQuantAmaxGrid = 2048;
 
 template <int D>
 __global__ void __launch_bounds__(256) fa_quant_codes_kernel(QuantArgs a) {
   using C = QuantCfg<D>;
   const int64_t row = (int64_t)blockIdx.x * C::RPB + threadIdx.x / C::L;
   const int lr = threadIdx.x % C::L;
-  float v[8];
+  float v[C::E];
   load_rotate<D>(a, row, lr, v);
   const float amax = __uint_as_float(*a.amax);
   const float descale = amax > 0.f ? amax / 448.f : 1.f;
+  const float inv = 1.f / descale;
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.descale = descale;
   if (row >= a.rows) return;
-  float y[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(e4m3_ready_quotient(v[e], descale), -448.f), 448.f);
-  u32x2 out;
-  out.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-      y[2], y[3], __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false), true);
-  out.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-      y[6], y[7], __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false), true);
-  *reinterpret_cast<u32x2*>(a.codes + row * D + 8 * lr) = out;
+  for (int c = 0; c < C::E / 16; ++c) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = fminf(fmaxf(e4m3_ready_quotient(v[16 * c + 4 * j + e], descale, inv), -448.f),
+                     448.f);
+      out[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+          y[2], y[3], __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false), true);
+    }
+    *reinterpret_cast<u32x4*>(a.codes + row * D + C::E * lr + 16 * c) = out;
+  }
 }
 
 template <int D>
@@ -147,7 +202,8 @@ static hipError_t launch_quant_t(const QuantArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fa_quant_clear_kernel, dim3(1), dim3(1), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_quant_amax_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((fa_quant_amax_kernel<D>), dim3((unsigned)min(grid, kQuantAmaxGrid)),
+                     dim3(C::NT), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((fa_quant_codes_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();

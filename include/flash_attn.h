@@ -172,7 +172,7 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
  *               Hadamard matrix); apply the same signs to Q and K (then
  *               Q M (K M)^T = Q K^T) and pass V with NULL.  Without, y = x.
  *   d         : 64 or 128
- * x needs 16-byte alignment, codes 16 bytes, descale and signs 4 bytes;
+ * x, codes and signs need 16-byte alignment, descale 4 bytes;
  * codes, descale and workspace must not overlap x, signs or each other.
  * rows = 0 is a no-op.  Three launches on `stream`.  Deterministic.
  */

@@ -211,7 +211,7 @@ def test_quantize_validation():
     assert _quant(lib, rows=-1) == SHAPE
     assert _quant(lib, d=96) == HEADDIM
     assert _quant(lib, x=None) == NULLP and _quant(lib, ws=None) == NULLP
-    assert _quant(lib, x=A + 8) == MISAL and _quant(lib, signs=5 * A + 2) == MISAL
+    assert _quant(lib, x=A + 8) == MISAL and _quant(lib, signs=5 * A + 4) == MISAL
     assert _quant(lib, wsb=2) == WS
     assert _quant(lib, codes=A + 16) == ALIAS                  # codes inside x
     assert _quant(lib, ws=3 * A) == ALIAS                      # workspace on descale
