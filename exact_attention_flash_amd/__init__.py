@@ -11,6 +11,7 @@ __all__ = [
     "flash_attn_fwd_splitkv",
     "flash_attn_fwd_fp8",
     "flash_attn_quantize_fp8",
+    "QUANT_WORKSPACE_BYTES",
     "flash_attn_fwd_dropout",
     "flash_attn_bwd_dropout",
     "flash_attn_fwd_splitkv_workspace_bytes",

@@ -181,6 +181,10 @@ def flash_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+# Workspace of flash_attn_quantize_fp8 (FA_QUANT_WORKSPACE_BYTES of the C header).
+QUANT_WORKSPACE_BYTES = 4096
+
+
 def flash_attn_quantize_fp8(x: torch.Tensor, signs: torch.Tensor | None = None,
                             codes: torch.Tensor | None = None, descale: torch.Tensor | None = None,
                             workspace: torch.Tensor | None = None, stream=None):
@@ -202,7 +206,8 @@ def flash_attn_quantize_fp8(x: torch.Tensor, signs: torch.Tensor | None = None,
             or codes.device != x.device:
         raise ValueError("codes must be a contiguous one-byte tensor of x's shape on x's device")
     descale = torch.empty(1, dtype=torch.float32, device=x.device) if descale is None else descale
-    workspace = torch.empty(1, dtype=torch.int32, device=x.device) if workspace is None else workspace
+    workspace = torch.empty(QUANT_WORKSPACE_BYTES // 4, dtype=torch.float32, device=x.device) \
+        if workspace is None else workspace
     lib = load_library()
     with torch.cuda.device(x.device):
         st = lib.flash_attn_quantize_fp8(x.data_ptr(), codes.data_ptr(), descale.data_ptr(),

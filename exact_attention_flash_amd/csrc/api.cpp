@@ -389,19 +389,21 @@ int flash_attn_quantize_fp8(const void* x, void* codes, float* descale, void* wo
   // grid: rows / (256 / (d / 8)) workgroups must fit a one-dimensional launch
   if ((rows + 15) / 16 > INT32_MAX) return FA_ERR_BAD_SHAPE;
   if (!x || !codes || !descale || !workspace) return FA_ERR_NULL_POINTER;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(descale, 4) || !aligned(workspace, 4) ||
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(descale, 4) || !aligned(workspace, 16) ||
       (signs && !aligned(signs, 16)))
     return FA_ERR_MISALIGNED;
-  if (workspace_bytes < 4) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < FA_QUANT_WORKSPACE_BYTES) return FA_ERR_WORKSPACE_TOO_SMALL;
   const size_t n = size_t(rows) * size_t(d);
   Range ins[2] = {range_of(x, 2 * n), range_of(signs, signs ? size_t(d) * 4 : 0)};
-  const Range outs[3] = {range_of(codes, n), range_of(descale, 4), range_of(workspace, 4)};
+  const Range outs[3] = {range_of(codes, n), range_of(descale, 4),
+                          range_of(workspace, FA_QUANT_WORKSPACE_BYTES)};
   if (any_alias(outs, 3, ins, signs ? 2 : 1)) return FA_ERR_ALIASING;
   fa::QuantArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.codes = static_cast<uint8_t*>(codes);
   a.descale = descale;
-  a.amax = static_cast<uint32_t*>(workspace);
+  a.part = static_cast<float*>(workspace);
+  static_assert(FA_QUANT_WORKSPACE_BYTES >= 4 * fa::kQuantParts, "quantise workspace");
   a.signs = signs;
   a.rows = rows;
   return fa::launch_quant_fp8(a, int(d), static_cast<hipStream_t>(stream)) == hipSuccess

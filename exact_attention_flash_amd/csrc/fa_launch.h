@@ -62,10 +62,14 @@ struct QuantArgs {
   const uint16_t* x;   // bf16 [rows, d]
   uint8_t* codes;      // E4M3 [rows, d]
   float* descale;      // out: amax / 448 (1 float)
-  uint32_t* amax;      // workspace: fp32 bits of the running amax
+  float* part;         // workspace: one partial amax per workgroup of the amax pass
   const float* signs;  // [d] of +-1, or nullptr (no rotation)
   int64_t rows;
+  int parts;           // set by the launcher: workgroups of the amax pass
 };
+
+// Largest number of partial maxima of the quantisation (workspace floats).
+constexpr int kQuantParts = 512;
 
 // Query rows per block of the backward key-block pass; the row vectors in
 // the backward workspace are padded to a multiple of it.
@@ -104,7 +108,7 @@ hipError_t launch_fwd_splitkv(const FwdArgs& a, int d, bool causal, hipStream_t 
 // Enqueue the FP8 forward kernel for head dim d (64 or 128).
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t stream);
 
-// Enqueue the FP8 quantisation (three launches) for head dim d (64 or 128).
+// Enqueue the FP8 quantisation (two launches) for head dim d (64 or 128).
 hipError_t launch_quant_fp8(const QuantArgs& a, int d, hipStream_t stream);
 
 // The three backward stages, each one kernel launch, for head dim d (64 or

@@ -166,16 +166,19 @@ int flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
  *   x         : in,  bf16 [rows, d] (e.g. Q or K as [B*H*N, d])
  *   codes     : out, E4M3 [rows, d]: codes of y / descale, nearest even
  *   descale   : out, device fp32 scalar: amax|y| / 448 (1 if y is all zero)
- *   workspace : device memory of at least 4 bytes, 4-byte aligned, no init
+ *   workspace : device memory of at least FA_QUANT_WORKSPACE_BYTES bytes,
+ *               16-byte aligned, no initialisation (partial maxima)
  *   signs     : device fp32 [d] of +1 / -1, or NULL.  With signs,
  *               y = x M, M = diag(signs) H_d / sqrt(d) (H_d the Sylvester
  *               Hadamard matrix); apply the same signs to Q and K (then
  *               Q M (K M)^T = Q K^T) and pass V with NULL.  Without, y = x.
  *   d         : 64 or 128
- * x, codes and signs need 16-byte alignment, descale 4 bytes;
+ * x, codes, signs and workspace need 16-byte alignment, descale 4 bytes;
  * codes, descale and workspace must not overlap x, signs or each other.
- * rows = 0 is a no-op.  Three launches on `stream`.  Deterministic.
+ * x must be finite.  rows = 0 is a no-op.  Two launches on `stream`.
+ * Deterministic.
  */
+#define FA_QUANT_WORKSPACE_BYTES 4096
 int flash_attn_quantize_fp8(const void* x, void* codes, float* descale,
                             void* workspace, size_t workspace_bytes,
                             int64_t rows, int64_t d, const float* signs, void* stream);

@@ -200,7 +200,7 @@ def test_dropout_validation():
     assert _bwd_drop(lib, p=0.0) == HIPERR
 
 
-def _quant(lib, x=A, codes=2 * A, ds=3 * A, ws=4 * A, wsb=4, rows=100, d=128, signs=5 * A):
+def _quant(lib, x=A, codes=2 * A, ds=3 * A, ws=4 * A, wsb=4096, rows=100, d=128, signs=5 * A):
     return lib.flash_attn_quantize_fp8(x, codes, ds, ws, wsb, rows, d, signs, None)
 
 
@@ -212,7 +212,8 @@ def test_quantize_validation():
     assert _quant(lib, d=96) == HEADDIM
     assert _quant(lib, x=None) == NULLP and _quant(lib, ws=None) == NULLP
     assert _quant(lib, x=A + 8) == MISAL and _quant(lib, signs=5 * A + 4) == MISAL
-    assert _quant(lib, wsb=2) == WS
+    assert _quant(lib, wsb=4095) == WS and _quant(lib, ws=4 * A + 4) == MISAL
+    assert _quant(lib, ws=3 * A - 4096 + 16) == ALIAS         # workspace runs into descale
     assert _quant(lib, codes=A + 16) == ALIAS                  # codes inside x
     assert _quant(lib, ws=3 * A) == ALIAS                      # workspace on descale
     assert _quant(lib, ds=5 * A) == ALIAS                      # descale on signs
