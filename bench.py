@@ -58,6 +58,8 @@ def parse_args():
     ap.add_argument("--fp8", action="store_true",
                     help="also time the FP8 (E4M3) forward next to the bf16 forward on the\n"
                          "fwd+bwd and long-context shapes; reported under 'fp8_forward'")
+    ap.add_argument("--naive", action="store_true",
+                    help="also time the materialise-S forward in bf16 torch ops on the same inputs")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters); not timed")
@@ -279,6 +281,47 @@ def dropout_measure(fa, tensors, wl, causal: bool, p: float, iters: int = 10) ->
     return out
 
 
+def naive_measure(q, k, v, o_fused, scale: float, causal: bool, f_fwd: float,
+                  iters: int = 5) -> dict:
+    """The materialise-S forward (the pages' plain PyTorch fallback: scores,
+    mask, softmax, product with V, each a separate kernel writing its full
+    N x N result) in bf16 torch ops on the GPU, timed with HIP events on the
+    current stream, for comparison with the fused forward on the same inputs.
+    Work is counted by the fused forward's convention."""
+    import torch
+    stream = torch.cuda.current_stream()
+    # torch's batched bf16 product is given a contiguous right operand, not a
+    # transposed view
+    kt = k.transpose(-1, -2).contiguous()
+    N = q.shape[-2]
+    mask = torch.ones(N, N, dtype=torch.bool, device=q.device).triu(1) if causal else None
+
+    def run():
+        s = torch.matmul(q, kt)
+        s.mul_(scale)
+        if causal:
+            s.masked_fill_(mask, float("-inf"))
+        p = torch.softmax(s, dim=-1)
+        del s
+        return torch.matmul(p, v)
+
+    o = run()
+    torch.cuda.synchronize()
+    diff = float((o.float() - o_fused.float()).abs().max())
+    del o
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"ms": round(ms, 4), "tflops": round(f_fwd / (ms * 1e-3) / 1e12, 2),
+            "max_abs_diff_vs_fused": round(diff, 5),
+            "note": "scores, mask, softmax and P V as separate bf16 torch kernels (N x N "
+                    "scores and probabilities written and read in HBM); forward only"}
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -412,6 +455,9 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.naive:
+        line["naive_fwd"] = naive_measure(q, k, v, o, scale, causal, f_fwd)
+        line["naive_fwd"]["fused_fwd_ms"] = round(avg_ms["fa_fwd"], 4)
     if args.splitkv > 0:
         line["splitkv"] = splitkv_measure(fa, make_inputs, args.splitkv)
     if args.dropout > 0:
