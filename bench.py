@@ -92,12 +92,22 @@ def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
     """The fp64 oracle on ``n_heads`` whole heads of the step, timed here."""
     import numpy as np
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = sum(int(p.get("num_threads", 1)) for p in threadpool_info()
-                    if p.get("user_api") == "blas") or 1
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = sum(int(p.get("num_threads", 1)) for p in pools) or 1
+        if pools:
+            blas = ", ".join(f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                             for p in pools)
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     n_heads = min(n_heads, wl.B * wl.H)
     stride = max(1, (wl.B * wl.H) // n_heads)
     heads = [divmod(i * stride, wl.H) for i in range(n_heads)]
@@ -113,8 +123,11 @@ def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu_model": cpu_model,
+        "blas": blas,
         "sample": (f"{len(heads)} of {wl.B * wl.H} heads of one step (forward + backward, "
-                   f"N={wl.N}, d={wl.d}, causal), float64 numpy, {dt:.2f} s; "
+                   f"N={wl.N}, d={wl.d}, {'causal' if causal else 'full'}), float64 numpy, "
+                   f"{dt:.2f} s; "
                    f"same flop convention as value"),
     }
 
@@ -394,8 +407,8 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
 
     names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_kv", "fa_bwd_q"]
-    avg_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps
-              for j, n in enumerate(names)}
+    times = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in events) for j, n in enumerate(names)}
+    avg_ms = {n: sum(t) / args.steps for n, t in times.items()}
     rows = B * H * N
     f_fwd, f_bwd = wl.flops_fwd(causal), wl.flops_bwd(causal)
     # (bound, algorithmic work per launch).  The backward's 2.5 x forward flop
@@ -413,7 +426,9 @@ def main() -> int:
         bound, w = work[n]
         t = avg_ms[n] * 1e-3
         ach = w / t / (1e12 if bound == "mfma" else 1e9)
-        kernels[n] = {"avg_ms": round(avg_ms[n], 4), "bound": bound,
+        kernels[n] = {"avg_ms": round(avg_ms[n], 4),
+                      "median_ms": round(times[n][len(times[n]) // 2], 4),
+                      "min_ms": round(times[n][0], 4), "bound": bound,
                       "achieved": round(ach, 2), "unit": "TFLOP/s" if bound == "mfma" else "GB/s"}
     dom = max(names, key=lambda n: avg_ms[n])
     bound, w = work[dom]
