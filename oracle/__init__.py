@@ -43,6 +43,7 @@ from .attention import (
     attention_forward,
     attention_forward_rows,
     attention_backward,
+    attention_backward_sampled,
 )
 from .fp8 import (
     decode_e4m3,
@@ -81,6 +82,7 @@ __all__ = [
     "attention_forward",
     "attention_forward_rows",
     "attention_backward",
+    "attention_backward_sampled",
     "decode_e4m3",
     "dequantize",
     "attention_forward_fp8",

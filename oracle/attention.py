@@ -200,3 +200,38 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool,
     if return_intermediates:
         return dQ, dK, dV, inter
     return dQ, dK, dV
+
+
+def attention_backward_sampled(q, k, v, dout, scale: float, causal: bool, rows, keys,
+                               row_chunk: int = 512):
+    """dQ for the query rows ``rows`` and dK, dV for the keys ``keys`` of one
+    head ``[N, d]``, without holding an N x N matrix.
+
+    The same calculus as ``attention_backward``, taken over complete query
+    rows a chunk at a time: for each row i, P_i and dP_i = dO_i V^T over all
+    N keys, dS_i by the per-row softmax Jacobian; dV_j = sum_i P_ij dO_i and
+    dK_j = scale sum_i dS_ij Q_i accumulate over the chunks for the listed
+    keys j, and dQ_i = scale dS_i K for the listed rows.  Rows are
+    independent and the sums over i only change their order, so this equals
+    the whole-head result on those rows and keys up to rounding.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    N, d = q.shape
+    sc = np.float64(scale)
+    dQ = np.empty((len(rows), d))
+    dK = np.zeros((len(keys), d))
+    dV = np.zeros((len(keys), d))
+    want = {int(r): n for n, r in enumerate(rows)}
+    R = max(1, int(row_chunk))
+    for r0 in range(0, N, R):
+        p = softmax_rows(scores(q[r0:r0 + R], k, scale, causal, r0))[2]
+        dp = do[r0:r0 + R] @ v.T
+        ds = softmax_row_grad(p, dp)
+        dV += p[:, keys].T @ do[r0:r0 + R]
+        dK += sc * (ds[:, keys].T @ q[r0:r0 + R])
+        for i in range(r0, min(r0 + R, N)):
+            if i in want:
+                dQ[want[i]] = sc * (ds[i - r0] @ k)
+    return dQ, dK, dV

@@ -305,3 +305,37 @@ def test_bwd_constant_v_gives_zero_dq_dk(d):
     gv = bf16_to_f64(dv)
     assert np.abs(bf16_to_f64(dq)).max() <= 5e-2 * np.abs(gv).max()
     assert np.abs(bf16_to_f64(dk)).max() <= 5e-2 * np.abs(gv).max()
+
+
+LONG = [
+    # (B, H, N, d, causal): a head 1.5 times as long as the longest named
+    # workload, and a long ragged one
+    (1, 1, 24576, 128, True),
+    (1, 1, 20001, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", LONG)
+def test_long_sequence_fwd_bwd(B, H, N, d, causal):
+    """Forward and backward on one long head, checked on sampled query rows
+    (O, LSE, dQ) and keys (dK, dV): block edges, the tail and random
+    positions, against the oracle's row-chunked backward."""
+    _say(f"long sequence ({B},{H},{N},{d}) causal={causal}")
+    x = make_inputs(B, H, N, d, seed=N + d, with_dout=True)
+    scale = default_scale(d)
+    (q, k, v), o, lse = _run_fwd(x, causal, scale)
+    do = to_device(x["do"])
+    dq, dk, dv = flash_attn_bwd(do, q, k, v, o, lse, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N)
+    idx = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, N // 2, N - 2, N - 1],
+                                    rng.choice(N, 29, replace=False)]))
+    xs = {n: x[n][0, 0] for n in ("q", "k", "v", "do")}
+    Or, Lr = oracle.attention_forward_rows(xs["q"], xs["k"], xs["v"], scale, causal, idx)
+    check_o(bf16_to_f64(o)[0, 0, idx], Or, "O")
+    check_lse(lse.cpu().numpy().astype(np.float64)[0, 0, idx], Lr, "LSE")
+    dQ, dK, dV = oracle.attention_backward_sampled(xs["q"], xs["k"], xs["v"], xs["do"], scale,
+                                                   causal, idx, idx)
+    check_grad(bf16_to_f64(dq)[0, 0, idx], dQ, "dQ")
+    check_grad(bf16_to_f64(dk)[0, 0, idx], dK, "dK")
+    check_grad(bf16_to_f64(dv)[0, 0, idx], dV, "dV")

@@ -106,3 +106,45 @@ def test_scale_enters_dq_dk_only():
     np.testing.assert_allclose(dV2, dV, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dK2, dK, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dQ2, dQ / c, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_matches_torch_autograd(causal):
+    """The row-chunked backward for a subset of rows and keys (used where a
+    whole N x N head would not fit) against torch fp64 autograd on the CPU,
+    a library routine, with chunks that split the head unevenly."""
+    rng = np.random.default_rng(11 + causal)
+    N, d = 37, 8
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    scale = 0.3
+    rows = np.array([0, 5, 17, 36])
+    keys = np.array([0, 1, 20, 36])
+    dQ, dK, dV = oracle.attention_backward_sampled(q, k, v, do, scale, causal, rows, keys,
+                                                   row_chunk=10)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    mask = torch.triu(torch.ones(N, N, dtype=torch.bool), 1) if causal else None
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt[None, None], kt[None, None], vt[None, None],
+        attn_mask=None if mask is None else ~mask, scale=scale)[0, 0]
+    o.backward(torch.tensor(do))
+    np.testing.assert_allclose(dQ, qt.grad.numpy()[rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, kt.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, vt.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+
+
+def test_sampled_backward_equals_whole_head():
+    """On a head small enough for the whole-head backward, the sampled one
+    gives the same rows and keys for every chunk size, including chunks of
+    one row and a single chunk."""
+    rng = np.random.default_rng(5)
+    N, d = 50, 16
+    q, k, v, do = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, 0.25, True)
+    rows = np.arange(0, N, 7)
+    keys = np.arange(3, N, 9)
+    for chunk in (1, 7, 50, 64):
+        sQ, sK, sV = oracle.attention_backward_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.25,
+                                                       True, rows, keys, row_chunk=chunk)
+        np.testing.assert_allclose(sQ, dQ[0, 0, rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sK, dK[0, 0, keys], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sV, dV[0, 0, keys], rtol=1e-12, atol=1e-13)

@@ -368,3 +368,49 @@ def test_rotation_pin_catches_planted_mistake(monkeypatch, target, bad, pin):
     monkeypatch.setattr(of8, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ---------------------------------------------------------------- sampled backward
+def _sampled_variant(no_scale=False, no_row_term=False, overwrite=False):
+    def f(q, k, v, dout, scale, causal, rows, keys, row_chunk=512):
+        q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+        rows, keys = np.asarray(rows), np.asarray(keys)
+        N, d = q.shape
+        sc = 1.0 if no_scale else scale
+        dQ = np.empty((len(rows), d))
+        dK = np.zeros((len(keys), d))
+        dV = np.zeros((len(keys), d))
+        for r0 in range(0, N, row_chunk):
+            p = oa.softmax_rows(oa.scores(q[r0:r0 + row_chunk], k, scale, causal, r0))[2]
+            dp = do[r0:r0 + row_chunk] @ v.T
+            ds = p * dp if no_row_term else oa.softmax_row_grad(p, dp)
+            if overwrite:
+                dV = p[:, keys].T @ do[r0:r0 + row_chunk]
+            else:
+                dV += p[:, keys].T @ do[r0:r0 + row_chunk]
+            dK += sc * (ds[:, keys].T @ q[r0:r0 + row_chunk])
+            for n, i in enumerate(rows):
+                if r0 <= i < r0 + row_chunk:
+                    dQ[n] = sc * (ds[i - r0] @ k)
+        return dQ, dK, dV
+    return f
+
+
+def _pin_sampled():
+    from tests.test_oracle_backward import test_sampled_backward_matches_torch_autograd
+    test_sampled_backward_matches_torch_autograd(True)
+
+
+MUTATIONS_SAMPLED = [
+    ("dK and dQ without the scale", _sampled_variant(no_scale=True)),
+    ("dS without the row term of the softmax Jacobian", _sampled_variant(no_row_term=True)),
+    ("dV overwritten by each row chunk", _sampled_variant(overwrite=True)),
+]
+
+
+@pytest.mark.parametrize("name,bad", MUTATIONS_SAMPLED, ids=[m[0] for m in MUTATIONS_SAMPLED])
+def test_sampled_backward_pin_catches_planted_mistake(monkeypatch, name, bad):
+    _pin_sampled()
+    monkeypatch.setattr(oracle, "attention_backward_sampled", bad)
+    with pytest.raises(AssertionError):
+        _pin_sampled()
