@@ -413,7 +413,6 @@ struct QBlock {
   f32x16 dq[D / 32];                // dQ^T: lane holds dQ[qrow][32 db + 8(i/4) + 4g + i%4]
   RowLane<D> rowk;                  // row reads of K / V (row swap23(c32) of each block)
   TrLane<D> trk;                    // transposed reads of K
-  uint32_t coff[C::COPIES];         // source offsets of the K / V tile copies
 
   // Copy t of thread (w, lane) fills 16-byte slot (t * NW + w) * 64 + lane of
   // a K / V tile (natural row order, chunk_swizzle chunks); its source byte
@@ -422,13 +421,12 @@ struct QBlock {
   __device__ __forceinline__ static int slot_row(int t, int w, int lane) {
     return ((t * C::NW + w) * 64 + lane) / C::CPR;
   }
-  __device__ __forceinline__ void init_copies() {
-#pragma unroll
-    for (int t = 0; t < C::COPIES; ++t) {
-      const int slot = (t * C::NW + w) * 64 + lane;
-      const int r = slot / C::CPR;
-      coff[t] = 2 * (r * D + (((slot % C::CPR) ^ chunk_swizzle<D>(r)) << 3));
-    }
+  // Computed at each use from an opaque lane index (a few integer
+  // operations per tile) rather than held in registers all kernel long.
+  __device__ __forceinline__ uint32_t copy_off(int t) const {
+    const int slot = (t * C::NW + w) * 64 + opaque(lane);
+    const int r = slot / C::CPR;
+    return 2 * (r * D + (((slot % C::CPR) ^ chunk_swizzle<D>(r)) << 3));
   }
 
   template <int ST>
@@ -441,8 +439,9 @@ struct QBlock {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t) {
         const int base = (t * C::NW + w) * 64 * 8;
-        buffer_load_lds16(kr, coff[t], ks[ST] + base);
-        buffer_load_lds16(vr, coff[t], vs[ST] + base);
+        const uint32_t off = copy_off(t);
+        buffer_load_lds16(kr, off, ks[ST] + base);
+        buffer_load_lds16(vr, off, vs[ST] + base);
       }
     } else {
 #pragma unroll
@@ -450,82 +449,118 @@ struct QBlock {
         const int base = (t * C::NW + w) * 64 * 8;
         const int r = slot_row(t, w, lane);
         const int shift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
-        buffer_load_lds16(kr, coff[t] + shift, ks[ST] + base);
-        buffer_load_lds16(vr, coff[t] + shift, vs[ST] + base);
+        const uint32_t off = copy_off(t) + shift;
+        buffer_load_lds16(kr, off, ks[ST] + base);
+        buffer_load_lds16(vr, off, vs[ST] + base);
       }
     }
+  }
+
+  // S^T and dP^T of 32-key block sb of the tile: value i of s[sb] is key
+  // k0 + 32 sb + 16 (i/8) + 8 g + i%8.
+  template <int ST>
+  __device__ __forceinline__ void scores(int sb, f32x16* s, f32x16* dp, const RowLane<D>& rk) {
+    const uint16_t* Ks = ks[ST];
+    const uint16_t* Vs = vs[ST];
+    s[sb] = zero16();
+    dp[sb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const int o = rk.off(32 * sb, kc);
+      s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + o), qf[kc], s[sb]);
+      dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + o), dof[kc], dp[sb]);
+    }
+    // keep the K / V reads two slices ahead of the MFMAs that consume them
+    sched_pipeline<D / 16, 2, 2, 2>();
+  }
+
+  // dS^T = P^T o (dP^T - D) of 32-key block sb, P^T = exp2(scale log2(e) S^T
+  // - LSE log2(e)), packed to bf16 as the B operands of 16-key chunks 2 sb
+  // and 2 sb + 1.
+  template <bool MASK>
+  __device__ __forceinline__ void softmax_ds(int sb, int k0, const f32x16* s, const f32x16* dp,
+                                             bf16x8* dsb) {
+    // dropout bytes of keys 32 sb + 16 h + 8 g + 0..7 (as in the forward pass:
+    // the lane draws 16-key group 2 sb + g and swaps half with the other
+    // wave half)
+    uint32_t rw[2][2];
+    if constexpr (DROP) {
+      const u32x4 own = philox4x32_10((uint32_t)(k0 >> 4) + 2 * sb + g, (uint32_t)qrow,
+                                      (uint32_t)bh, drop.offset, drop.k0, drop.k1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(own[e], own[2 + e], false, false);
+        rw[0][e] = r[0];
+        rw[1][e] = r[1];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float t8[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i = 8 * h + jj;
+        float pv = exp2_fast(fmaf(s[sb][i], sl2, -lse2));
+        if constexpr (MASK) {
+          const int key = k0 + 32 * sb + 16 * h + 8 * g + jj;
+          if (key >= N || (CAUSAL && key > qrow)) pv = 0.f;
+        }
+        if constexpr (DROP) {
+          const bool keep = drop_keep(rw[h][jj >> 2], jj & 3, drop.t);
+          t8[jj] = pv * fmaf(dp[sb][i], keep ? drop.scale : 0.f, -dlt);
+        } else {
+          t8[jj] = pv * (dp[sb][i] - dlt);
+        }
+      }
+      dsb[2 * sb + h] = pack8(t8);
+    }
+  }
+
+  // dQ^T += K^T dS^T over 16-key chunk kc2 of the tile (K^T read transposed).
+  template <int ST>
+  __device__ __forceinline__ void dq_chunk(int kc2, const bf16x8* dsb, const TrLane<D>& tr) {
+    const uint16_t* Ks = ks[ST];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x8 ka = join_tr(lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 0)),
+                                lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 1)));
+      dq[db] = mfma32(ka, dsb[kc2], dq[db]);
+    }
+  }
+
+  // One tile, ordered so that each block's exponentials and dS run beside
+  // independent MFMAs of the same wave (an MFMA issues and executes while
+  // the wave goes on issuing vector instructions): block 1's S and dP beside
+  // block 0's softmax, the dQ products of block 0's chunks beside block 1's.
+  // MASK: the tile straddles the diagonal or the end of the sequence.
+  template <int ST, bool MASK>
+  __device__ __forceinline__ void tile(int j) {
+    static_assert(BC == 64, "two 32-key blocks per tile");
+    const int k0 = j * BC;
+    const RowLane<D> rk = rowk.fresh();
+    const TrLane<D> tr = trk.fresh();
+    f32x16 s[2], dp[2];
+    bf16x8 dsb[4];
+    // scheduling regions; the compiler interleaves within each
+    scores<ST>(0, s, dp, rk);
+    __builtin_amdgcn_sched_barrier(0);
+    scores<ST>(1, s, dp, rk);
+    softmax_ds<MASK>(0, k0, s, dp, dsb);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_ds<MASK>(1, k0, s, dp, dsb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kc2 = 0; kc2 < 4; ++kc2) dq_chunk<ST>(kc2, dsb, tr);
   }
 
   template <int ST>
   __device__ __forceinline__ void step(int j) {
     if (j + 1 < nt) issue<ST ^ 1>(j + 1);
-    const uint16_t* Ks = ks[ST];
-    const uint16_t* Vs = vs[ST];
     const int k0 = j * BC;
     if (!(CAUSAL && (k0 > qw0 + C::QW - 1))) {
-      const RowLane<D> rk = rowk.fresh();
-      const TrLane<D> tr = trk.fresh();
-      // S^T, dP^T: value i of s[sb] is key k0 + 32 sb + 16 (i/8) + 8 g + i%8
-      f32x16 s[BC / 32], dp[BC / 32];
-#pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb) { s[sb] = zero16(); dp[sb] = zero16(); }
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc)
-#pragma unroll
-        for (int sb = 0; sb < BC / 32; ++sb) {
-          const int o = rk.off(32 * sb, kc);
-          s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + o), qf[kc], s[sb]);
-          dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + o), dof[kc], dp[sb]);
-        }
-      // keep the K / V reads two slices ahead of the MFMAs that consume them
-      sched_pipeline<D / 16, 2 * (BC / 32), 2 * (BC / 32), 2>();
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
-      // dropout bytes of keys 16 n + 8 g + 0..7 (as in the forward pass: the
-      // lane draws 16-key group 2 m + g and swaps half with the other wave half)
-      uint32_t rw[BC / 16][2];
-      if constexpr (DROP) {
-#pragma unroll
-        for (int m = 0; m < BC / 32; ++m) {
-          const u32x4 own = philox4x32_10((uint32_t)(k0 >> 4) + 2 * m + g, (uint32_t)qrow,
-                                          (uint32_t)bh, drop.offset, drop.k0, drop.k1);
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const auto r = __builtin_amdgcn_permlane32_swap(own[e], own[2 + e], false, false);
-            rw[2 * m][e] = r[0];
-            rw[2 * m + 1][e] = r[1];
-          }
-        }
-      }
-#pragma unroll
-      for (int sb = 0; sb < BC / 32; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = exp2_fast(fmaf(s[sb][i], sl2, -lse2));
-          if (need_mask) {
-            const int key = k0 + 32 * sb + 16 * (i >> 3) + 8 * g + (i & 7);
-            if (key >= N || (CAUSAL && key > qrow)) pv = 0.f;
-          }
-          if constexpr (DROP) {
-            const bool keep = drop_keep(rw[2 * sb + (i >> 3)][(i & 7) >> 2], i & 3, drop.t);
-            s[sb][i] = pv * fmaf(dp[sb][i], keep ? drop.scale : 0.f, -dlt);  // dS^T
-          } else {
-            s[sb][i] = pv * (dp[sb][i] - dlt);  // dS^T
-          }
-        }
-      // dQ^T += K^T dS^T over the tile's four 16-key chunks.
-#pragma unroll
-      for (int kc2 = 0; kc2 < BC / 16; ++kc2) {
-        float t8[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) t8[jj] = s[kc2 >> 1][(kc2 & 1) * 8 + jj];
-        const bf16x8 dsb = pack8(t8);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ka = join_tr(lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 0)),
-                                    lds_read_tr(Ks + tr.off(16 * kc2, 32 * db, 1)));
-          dq[db] = mfma32(ka, dsb, dq[db]);
-        }
-      }
+      if (need_mask) tile<ST, true>(j);
+      else tile<ST, false>(j);
     }
     wait_vmem();
     __syncthreads();
@@ -573,7 +608,6 @@ fa_bwd_q_kernel(BwdArgs a) {
   f.sl2 = a.scale_log2;
   f.rowk = RowLane<D>(f.lane);
   f.trk = TrLane<D>(f.lane);
-  f.init_copies();
 
   f.template issue<0>(0);
   const bool real = f.qrow < N;
