@@ -339,7 +339,7 @@ def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; --gpus N > 1 is not supported "
+        print("bench.py: measures one GPU only; --gpus N > 1 is not supported "
               "(the path shards over (batch, head) with no exchange between GPUs)",
               file=sys.stderr)
         return 2

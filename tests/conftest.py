@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # A gpu-marked test never runs silently on a machine without a GPU: it is
-    # skipped with the reason, and `-m gpu` on a GPU machine runs it for real.
+    # skipped with the reason, and `-m gpu` on a machine with a GPU runs it.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
