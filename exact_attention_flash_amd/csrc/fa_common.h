@@ -373,6 +373,20 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// The same for a wave-uniform value in a scalar register: sums built on it
+// at each use (an LDS destination per copy, say) cost one scalar add there
+// instead of a scalar register each for the whole kernel.
+__device__ __forceinline__ int opaque_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+template <typename T>
+__device__ __forceinline__ const T* opaque_s(const T* p) {
+  uint32_t lo = (uint32_t)(uintptr_t)p, hi = (uint32_t)((uintptr_t)p >> 32);
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return reinterpret_cast<const T*>((uintptr_t)lo | ((uintptr_t)hi << 32));
+}
+
 // Per-lane constants for transposed reads (lds_read_tr) of a swizzled
 // row-major [rows][D] tile, as MFMA operands with rows = contraction index:
 // the read for row block R0 (a multiple of 16), column block C0 (a multiple

@@ -106,10 +106,11 @@ struct TileCopy {
 #pragma unroll
       for (int e = 0; e < 2; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);
     }
+    const int wb = opaque_s(w * 64 * 8);  // this wave's slots
     if (k0 + C::BC <= N) {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t)
-        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + (t * C::NW + w) * 64 * 8);
+        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + t * C::NW * 64 * 8 + wb);
     } else {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t) {
@@ -117,7 +118,7 @@ struct TileCopy {
         const int r = opaque(KEYS ? swap23(slot_row(t, w, lane)) : slot_row(t, w, lane));
         const int shift = (min(k0 + r, N - 1) - (k0 + r)) * D * 2;
         buffer_load_lds16_unseen(rs, (KEYS ? koff[t] : voff[t]) + shift,
-                                 Ts + (t * C::NW + w) * 64 * 8);
+                                 Ts + t * C::NW * 64 * 8 + wb);
       }
     }
   }

@@ -142,18 +142,21 @@ struct Fp8TileCopy {
   template <bool KEYS>
   __device__ __forceinline__ void issue(const uint8_t* X, uint8_t* Ts, int k0, int N, int w,
                                         int lane) const {
-    const i32x4 rs = make_rsrc_words(X + (int64_t)k0 * D, C::TILE);
+    // the resource is rebuilt from the laundered head pointer at each issue,
+    // so that its words do not sit in scalar registers across the loop
+    const i32x4 rs = make_rsrc_words(opaque_s(X) + (int64_t)k0 * D, C::TILE);
+    const int wb = opaque_s(w * 64 * 16);  // this wave's slots
     if (k0 + C::BC <= N) {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t)
-        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + (t * C::NW + w) * 64 * 16);
+        buffer_load_lds16_unseen(rs, KEYS ? koff[t] : voff[t], Ts + t * C::NW * 64 * 16 + wb);
     } else {
 #pragma unroll
       for (int t = 0; t < C::COPIES; ++t) {
         const int r = opaque(slot_row(t, w, lane));
         const uint32_t shift = (uint32_t)((min(k0 + r, N - 1) - (k0 + r)) * D);
         buffer_load_lds16_unseen(rs, (KEYS ? koff[t] : voff[t]) + shift,
-                                 Ts + (t * C::NW + w) * 64 * 16);
+                                 Ts + t * C::NW * 64 * 16 + wb);
       }
     }
   }
