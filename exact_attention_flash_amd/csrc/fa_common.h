@@ -63,11 +63,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // log2 on the transcendental unit, for positive normal inputs.
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value of lane (lane ^ 32): swaps the two 32-lane halves of the wave.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
 // max(x[lane], x[lane ^ 32]) and x[lane] + x[lane ^ 32] with one
 // v_permlane32_swap (gfx950): swapping one wave half of x against the other
 // leaves the two values of each lane pair in the two results.
@@ -143,89 +138,6 @@ namespace fa {
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-
-// Select the low (hi == 0) or high 16-bit halves of two words into one word:
-// result = { a.half, b.half }.
-__device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int hi) {
-  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
-
-// ROWS x D bf16 tile of a row-major [N, D] matrix, staged global -> registers
-// -> LDS without transposition.  Rows at or beyond N read as zero.  LDS row
-// r holds source row swap23(r) when PERMUTE is set.
-template <int ROWS, int D, int NT, bool PERMUTE>
-struct RowTile {
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int TASKS = ROWS * CPR;
-  static constexpr int PER = (TASKS + NT - 1) / NT;
-  u32x4 r[PER];
-
-  __device__ __forceinline__ void load(const uint16_t* base, int r0, int N, int tid) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int t = p * NT + tid;
-      const int row = t / CPR, ch = t % CPR;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (t < TASKS && r0 + row < N)
-        z = load_global<u32x4>(base + (int64_t)(r0 + row) * D + ch * 8);
-      r[p] = z;
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int pitch, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int t = p * NT + tid;
-      if (t < TASKS) {
-        const int row = t / CPR, ch = t % CPR;
-        const int lr = PERMUTE ? swap23(row) : row;
-        *reinterpret_cast<u32x4*>(lds + lr * pitch + ch * 8) = r[p];
-      }
-    }
-  }
-};
-
-// ROWS x D bf16 tile stored transposed in LDS ([D][ROWS], row pitch `pitch`
-// elements).  Each task owns four consecutive source rows of one 8-column
-// chunk and writes eight 8-byte runs (four rows of one column each).
-template <int ROWS, int D, int NT>
-struct TransTile {
-  static constexpr int GROUPS = ROWS / 4;
-  static constexpr int TASKS = GROUPS * (D / 8);
-  static constexpr int PER = (TASKS + NT - 1) / NT;
-  u32x4 r[PER][4];
-
-  __device__ __forceinline__ void load(const uint16_t* base, int r0, int N, int tid) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int t = p * NT + tid;
-      const int kg = t % GROUPS, ch = t / GROUPS;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = r0 + 4 * kg + u;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (t < TASKS && row < N) z = load_global<u32x4>(base + (int64_t)row * D + ch * 8);
-        r[p][u] = z;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int pitch, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int t = p * NT + tid;
-      if (t < TASKS) {
-        const int kg = t % GROUPS, ch = t / GROUPS;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1, hi = e & 1;
-          u32x2 val;
-          val.x = pick_halves(r[p][0][w], r[p][1][w], hi);
-          val.y = pick_halves(r[p][2][w], r[p][3][w], hi);
-          *reinterpret_cast<u32x2*>(lds + (ch * 8 + e) * pitch + 4 * kg) = val;
-        }
-      }
-    }
-  }
-};
 
 }  // namespace fa
 
@@ -314,9 +226,6 @@ __device__ __forceinline__ void wait_vmem_except_last() {
   asm volatile("" ::: "memory");
 }
 
-// Keep the compiler from moving memory operations across this point.
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
 // gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane 4e + q supplies the address of 4 consecutive 16-bit values;
 // lane i of the group receives element i % 4 of the run supplied by lane
@@ -352,12 +261,6 @@ __device__ __forceinline__ int chunk_swizzle(int row) {
     return ((row & 1) ? 0x2 : 0) ^ ((row & 2) ? 0x4 : 0) ^ ((row & 4) ? 0x1 : 0) ^
            ((row & 8) ? 0x2 : 0);
   }
-}
-
-// Element offset of (row, col) in a swizzled [rows][D] bf16 tile.
-template <int D>
-__device__ __forceinline__ int swz_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ chunk_swizzle<D>(row))) << 3) + (col & 7);
 }
 
 }  // namespace fa
