@@ -339,3 +339,59 @@ def test_long_sequence_fwd_bwd(B, H, N, d, causal):
     check_grad(bf16_to_f64(dq)[0, 0, idx], dQ, "dQ")
     check_grad(bf16_to_f64(dk)[0, 0, idx], dK, "dK")
     check_grad(bf16_to_f64(dv)[0, 0, idx], dV, "dV")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", ["rising", "falling", "large"])
+def test_fwd_extreme_logits(d, causal, pattern):
+    """The lazy running max under stress: scores that rise along the keys by
+    more than the rescale threshold per key tile (the max moves on every
+    tile), scores that fall along the keys (it never moves after the first),
+    and random logits reaching ~350 (Q scaled by 64, exact in bf16); all
+    against the oracle."""
+    from exact_attention_flash_amd.inputs import f32_to_bf16_bits
+    _say(f"extreme logits {pattern} d={d} causal={causal}")
+    B, H, N = 1, 2, 700
+    x = make_inputs(B, H, N, d, seed=13 + d)
+    rng = np.random.default_rng(d + causal)
+    scale = default_scale(d)
+    if pattern == "large":
+        q = oracle.widen_bf16(x["q"]).astype(np.float32) * 64.0
+        x["q"] = f32_to_bf16_bits(q)
+    else:
+        u = rng.standard_normal(d).astype(np.float32)
+        u /= np.linalg.norm(u)
+        ramp = np.linspace(0.0, 1.0, N, dtype=np.float32)
+        if pattern == "falling":
+            ramp = ramp[::-1].copy()
+        # s_ij = scale * (q_i . u) * c * ramp_j with q_i . u = 1: spans 0 .. 3000
+        c = np.float32(3000.0 / scale)
+        q = np.broadcast_to(u, (B, H, N, d)) + 0.01 * rng.standard_normal((B, H, N, d))
+        k = (c * ramp)[None, None, :, None] * u[None, None, None, :] \
+            + 0.01 * rng.standard_normal((B, H, N, d))
+        x["q"] = f32_to_bf16_bits(q.astype(np.float32))
+        x["k"] = f32_to_bf16_bits(k.astype(np.float32))
+    x["do"] = make_inputs(B, H, N, d, seed=77 + d, with_dout=True)["do"]
+    (q, k, v), o, lse = _run_fwd(x, causal, scale)
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    check_o(bf16_to_f64(o), O_ref, f"O ({pattern})")
+    # Backward on the same inputs.  P is close to one-hot here, so the exact
+    # dS = P (dP - D) nearly vanishes while the bf16 rounding of O (which
+    # forms D = rowsum(dO * O)) moves it by ~2^-9 |dO . O|: dQ and dK are
+    # ill-conditioned against a bar relative to their own maximum and are
+    # only checked for finiteness; dV = P^T dO is well-conditioned.
+    dq, dk, dv = flash_attn_bwd(to_device(x["do"]), q, k, v, o, lse, causal=causal,
+                                softmax_scale=scale)
+    torch.cuda.synchronize()
+    _, _, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    check_grad(bf16_to_f64(dv), dV, f"dV ({pattern})")
+    assert np.all(np.isfinite(bf16_to_f64(dq))) and np.all(np.isfinite(bf16_to_f64(dk)))
+    l64 = lse.cpu().numpy().astype(np.float64)
+    # Scores reach ~3000 here. Each fp32 rounding on the way to the LSE (the
+    # dot product's accumulation, the scale and base-2 conversions, the max
+    # and the final log) costs up to 2^-24 of that magnitude: allow 32 of
+    # them on top of the usual 1e-3.
+    assert np.all(np.isfinite(l64))
+    bound = 1e-3 + 32 * 2.0 ** -24 * np.abs(L_ref).max()
+    assert np.abs(l64 - L_ref).max() <= bound, (np.abs(l64 - L_ref).max(), bound)
