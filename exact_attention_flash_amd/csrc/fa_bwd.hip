@@ -18,8 +18,12 @@
 // Three kernels on the caller's stream:
 //   fa_bwd_pre   D = rowsum(dO o O) and LSE * log2(e), padded to whole
 //                64-row query blocks (D = 0, LSE = +inf on padding rows)
-//   fa_bwd_kv    one workgroup per (batch, head, 128-key block): dK, dV
+//   fa_bwd_kv    persistent: one workgroup per CU walks its share of the
+//                (batch, head, 128-key block) items: dK, dV
 //   fa_bwd_q     one workgroup per (batch, head, 128-query block): dQ
+#include <algorithm>
+#include <atomic>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -129,6 +133,26 @@ struct KvSmem {
   uint8_t* drop;  // dropout bytes, 1 KiB per wave (DROP only)
 };
 
+// The items (head, key block) of the persistent key-block pass: round r of
+// workgroup b takes item(r).  With the item count and the grid both multiples
+// of 8, workgroup b stays on the XCD of its items (b mod 8, as consecutive
+// workgroups are placed round robin over the 8 XCDs) and walks that XCD's
+// list in snake order (forward in even rounds, backward in odd ones), which
+// pairs the heavy early causal key blocks with light late ones; otherwise
+// round robin over all items.
+struct ItemWalk {
+  int b, G, total;
+  __device__ __forceinline__ int item(int r) const {
+    if (((total | G) & 7) == 0) {
+      const int g = G >> 3, c = b >> 3;
+      const int j = r * g + ((r & 1) ? g - 1 - c : c);
+      return j < (total >> 3) ? 8 * j + (b & 7) : -1;
+    }
+    const int L = b + r * G;
+    return L < total ? L : -1;
+  }
+};
+
 // One workgroup of the key-block pass (8 waves, 16 keys each).  S = Q K^T,
 // dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS use v_mfma_f32_16x16x32_bf16
 // with a lane owning one key; the 16 queries of an S tile are fed in the
@@ -141,36 +165,27 @@ struct KvBlock {
 
   const KvSmem sm;
   const BwdArgs& a;
-  int w, lane, c16, kg, N, kb0, kw0, key, nqb, bh;
+  int w, lane, c16, kg, N, nqb;
+  int bh, kb0, kw0, key;  // the current item: head, first key, this wave's keys, lane's key
   int64_t hoff;
-  const uint16_t* Qh;
-  const uint16_t* dOh;
-  const float* lse2h;
-  const float* delh;
+  int nbh, nkb0;          // the next item of this workgroup (nbh < 0: none)
+  int round;              // index of the current item in the workgroup's walk
   float sl2;
   int srow_base, srow_u;  // 16-byte row reads of Q / dO for S and dP
   int tq_base, tq_t;      // transposed reads of Q / dO for dK and dV
   QTileCopy<D> cp;                // source offsets of the Q / dO tile copies
-  bf16x8 kf[D / 32], vf[D / 32];  // B operands: K, V rows of this lane's key
-  f32x4 dk[D / 16], dv[D / 16];   // dK^T, dV^T: lane holds [16 dt + 4 kg + i][key]
+  bf16x8 kf[D / 32], vf[D / 32];    // B operands: K, V rows of this lane's key
+  bf16x8 kfn[D / 32], vfn[D / 32];  // the same rows of the next item, loaded ahead
+  f32x4 dk[D / 16], dv[D / 16];     // dK^T, dV^T: lane holds [16 dt + 4 kg + i][key]
 
-  __device__ __forceinline__ KvBlock(const KvSmem& sm_, const BwdArgs& a_, int bh, int kb0_)
-      : sm(sm_), a(a_), bh(bh) {
+  __device__ __forceinline__ KvBlock(const KvSmem& sm_, const BwdArgs& a_) : sm(sm_), a(a_) {
     const int tid = threadIdx.x;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     lane = tid & 63;
     c16 = lane & 15;
     kg = lane >> 4;
     N = a.N;
-    kb0 = kb0_;
-    kw0 = kb0 + w * C::KW;
-    key = kw0 + c16;
     nqb = (N + BRQ - 1) / BRQ;
-    hoff = (int64_t)bh * N * D;
-    Qh = a.q + hoff;
-    dOh = a.dout + hoff;
-    lse2h = a.lse2 + (int64_t)bh * a.Npad;
-    delh = a.delta + (int64_t)bh * a.Npad;
     sl2 = a.scale_log2;
     // row of S tile t in 32-query group qg fed by lane c16:
     // 32 qg + 8 (c16 / 4) + 4 t + c16 % 4 (t and qg do not change the swizzle)
@@ -186,26 +201,59 @@ struct KvBlock {
     cp.init(w, lane);
   }
 
-  __device__ __forceinline__ void load_kv_operands() {
+  // First query block that item (head, key block from kb0_) visits.
+  __device__ __forceinline__ int first_block(int kb0_) const { return CAUSAL ? kb0_ / BRQ : 0; }
+
+  __device__ __forceinline__ void set_item(int bh_, int kb0_) {
+    bh = bh_;
+    kb0 = kb0_;
+    kw0 = kb0 + w * C::KW;
+    key = kw0 + c16;
+    hoff = (int64_t)bh * N * D;
+  }
+
+  // Item L of the walk, or nbh = -1 past its end.
+  __device__ __forceinline__ void plan_next(const ItemWalk& walk, int nkb) {
+    const int L = walk.item(round + 1);
+    if (L < 0) {
+      nbh = -1;
+      return;
+    }
+    int kb;
+    xcd_head_block<kHeadsPerGroup>(L, walk.total, a.BH, nkb, nbh, kb);
+    nkb0 = kb * BCK;
+  }
+
+  // K and V rows of this lane's key of item (bh_, kb0_) (zero past N).
+  __device__ __forceinline__ void load_rows(bf16x8 (&kd)[D / 32], bf16x8 (&vd)[D / 32], int bh_,
+                                            int kb0_) const {
+    const int ky = kb0_ + w * C::KW + c16;
+    const int64_t ho = (int64_t)bh_ * N * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const int64_t off = hoff + (int64_t)key * D + 32 * s + 8 * kg;
-      kf[s] = key < N ? load_global<bf16x8>(a.k + off) : zero_bf16x8();
-      vf[s] = key < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
+      const int64_t off = ho + (int64_t)ky * D + 32 * s + 8 * kg;
+      kd[s] = ky < N ? load_global<bf16x8>(a.k + off) : zero_bf16x8();
+      vd[s] = ky < N ? load_global<bf16x8>(a.v + off) : zero_bf16x8();
     }
+  }
+
+  __device__ __forceinline__ void zero_acc() {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) { dk[dt] = zero4(); dv[dt] = zero4(); }
   }
 
+  // Copies of query block i of head bh_ into stage ST.
   template <int ST>
-  __device__ __forceinline__ void issue_q(int i) {
+  __device__ __forceinline__ void issue_q(int bh_, int i) {
     const int q0 = i * BRQ;
-    cp.issue(Qh, dOh, sm.q[ST], sm.dout[ST], q0, N, w, lane);
+    const int64_t ho = (int64_t)bh_ * N * D;
+    cp.issue(a.q + ho, a.dout + ho, sm.q[ST], sm.dout[ST], q0, N, w, lane);
     // LSE*log2(e) then D of the block: 2 x BRQ floats = BRQ / 2 lanes of 16
     // bytes (the rows are padded to whole blocks)
     if (w == 0 && lane < BRQ / 2) {
       constexpr int half = BRQ / 4;  // lanes per vector
-      const float* src = lane < half ? lse2h + q0 + 4 * lane : delh + q0 + 4 * (lane - half);
+      const int64_t vo = (int64_t)bh_ * a.Npad + q0;
+      const float* src = lane < half ? a.lse2 + vo + 4 * lane : a.delta + vo + 4 * (lane - half);
       load_lds16(src, sm.vec[ST]);
     }
   }
@@ -303,13 +351,40 @@ struct KvBlock {
     }
   }
 
-  // Block i from stage ST, with block i + 1 prefetched into the other stage.
+  // Block i of the current item from stage ST, with the next block (of this
+  // item, else the first of the next item, whose K and V rows are loaded at
+  // the same time) prefetched into the other stage.  After an item's last
+  // block: dK and dV are stored and the next item takes over.  Returns false
+  // once the walk is done.
   template <int ST>
-  __device__ __forceinline__ void step(int i) {
-    if (i + 1 < nqb) issue_q<ST ^ 1>(i + 1);
+  __device__ __forceinline__ bool step(int& i, const ItemWalk& walk, int nkb) {
+    const bool last = i + 1 == nqb;
+    if (!last) {
+      issue_q<ST ^ 1>(bh, i + 1);
+    } else if (nbh >= 0) {
+      issue_q<ST ^ 1>(nbh, first_block(nkb0));
+      load_rows(kfn, vfn, nbh, nkb0);
+    }
     block<ST>(i);
     wait_vmem();
     __syncthreads();
+    if (!last) {
+      ++i;
+      return true;
+    }
+    store();
+    if (nbh < 0) return false;
+    set_item(nbh, nkb0);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      kf[s] = kfn[s];
+      vf[s] = vfn[s];
+    }
+    zero_acc();
+    i = first_block(kb0);
+    ++round;
+    plan_next(walk, nkb);
+    return true;
   }
 
   __device__ __forceinline__ void store() {
@@ -353,26 +428,25 @@ fa_bwd_kv_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkb = (N + C::BCK - 1) / C::BCK;
-  // Workgroup -> (head, key block): heads grouped per XCD; causal key blocks
-  // near the start see the most query blocks, so run order is already
-  // heaviest first.
+  // Items (head, key block) in run order: heads grouped per XCD; causal key
+  // blocks near the start see the most query blocks, so run order 0 is the
+  // heaviest.  The grid (at most one workgroup per CU, never more than the
+  // items) walks them.
+  const ItemWalk walk{(int)blockIdx.x, (int)gridDim.x, a.BH * nkb};
+  KvBlock<D, CAUSAL, DROP> blk(sm, a);
   int bh, kb;
-  xcd_head_block<kHeadsPerGroup>(blockIdx.x, gridDim.x, a.BH, nkb, bh, kb);
-
-  KvBlock<D, CAUSAL, DROP> blk(sm, a, bh, kb * C::BCK);
-  const int nqb = blk.nqb;
-  const int i0 = CAUSAL ? blk.kb0 / C::BRQ : 0;
-  blk.template issue_q<0>(i0);
-  blk.load_kv_operands();
+  xcd_head_block<kHeadsPerGroup>(walk.item(0), walk.total, a.BH, nkb, bh, kb);
+  blk.set_item(bh, kb * C::BCK);
+  blk.round = 0;
+  blk.plan_next(walk, nkb);
+  int i = blk.first_block(blk.kb0);
+  blk.template issue_q<0>(bh, i);
+  blk.load_rows(blk.kf, blk.vf, bh, blk.kb0);
+  blk.zero_acc();
   wait_vmem();
   __syncthreads();
-  int i = i0;
-  for (; i + 1 < nqb; i += 2) {
-    blk.template step<0>(i);
-    blk.template step<1>(i + 1);
+  while (blk.template step<0>(i, walk, nkb) && blk.template step<1>(i, walk, nkb)) {
   }
-  if (i < nqb) blk.template step<0>(i);
-  blk.store();
 }
 
 // ------------------------------------------------------------------ query-block pass
@@ -657,12 +731,29 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int D, bool CAUSAL, bool DROP = false>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t stream) {
   using C = KvCfg<D>;
-  const int64_t nkb = (a.N + C::BCK - 1) / C::BCK;
-  hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL, DROP>), dim3((unsigned)(nkb * a.BH)), dim3(C::NT),
-                     0, stream, a);
+  const int64_t items = (int64_t)((a.N + C::BCK - 1) / C::BCK) * a.BH;
+  // one workgroup per CU (the kernel's registers allow no more), a multiple
+  // of 8 so that each stays on the XCD of its items; all items if fewer
+  const int cus = cu_count();
+  int64_t grid = cus > 0 ? std::min<int64_t>(items, cus) : items;
+  if (grid >= 8) grid &= ~int64_t(7);
+  hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
