@@ -212,13 +212,18 @@ struct FwdWave {
     const int k0 = (t0 + t) * BC;
     const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
     if (need_mask) {
-      // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset)
+      // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset).
+      // The select is bit arithmetic on a sign mask kept opaque, so that it
+      // stays in vector registers instead of 32 live compare masks in
+      // scalar register pairs.
       const int lim = opaque((CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 8 * g);
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * sb + 16 * (i >> 3) + (i & 7) > lim) s[sb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t hide = (uint32_t)opaque((lim - (32 * sb + 16 * (i >> 3) + (i & 7))) >> 31);
+          s[sb][i] = __uint_as_float((__float_as_uint(s[sb][i]) & ~hide) | (0xff800000u & hide));
+        }
     }
     float mx = -INFINITY;
 #pragma unroll

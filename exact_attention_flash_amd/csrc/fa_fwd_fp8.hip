@@ -244,12 +244,17 @@ struct Fp8Wave {
     if (need_mask) {
       // key k0 + 32 sb + 8 (i / 4) + 4 g + i % 4 is visible iff its offset
       // from k0 + 4 g is <= lim
+      // The select is bit arithmetic on a sign mask kept opaque, so that it
+      // stays in vector registers instead of 64 live compare masks in scalar
+      // register pairs.
       const int lim = opaque((CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 4 * g);
 #pragma unroll
       for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * sb + 8 * (i >> 2) + (i & 3) > lim) s[sb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t hide = (uint32_t)opaque((lim - (32 * sb + 8 * (i >> 2) + (i & 3))) >> 31);
+          s[sb][i] = __uint_as_float((__float_as_uint(s[sb][i]) & ~hide) | (0xff800000u & hide));
+        }
     }
     // row max in four independent chains (a single chain of dependent
     // v_max3 is latency bound)
