@@ -395,3 +395,40 @@ def test_fwd_extreme_logits(d, causal, pattern):
     assert np.all(np.isfinite(l64))
     bound = 1e-3 + 32 * 2.0 ** -24 * np.abs(L_ref).max()
     assert np.abs(l64 - L_ref).max() <= bound, (np.abs(l64 - L_ref).max(), bound)
+
+
+WALKS = [
+    # (B, H, N, d, causal) and the key-block walk each gives on a 256-CU
+    # device (one workgroup per CU, 128-key items):
+    (1, 8, 5000, 128, True),   # 320 items: snake order, partial second round
+    (1, 8, 5000, 64, False),   # the same walk, full attention, d = 64
+    (3, 5, 2100, 128, True),   # 255 items on 248 workgroups: round robin, 7 take two
+    (2, 20, 4096, 64, True),   # 1280 items: snake order over five rounds
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", WALKS)
+def test_bwd_key_block_walk(B, H, N, d, causal):
+    """Backward where the persistent key-block pass gives workgroups several
+    items (and an odd number of rounds, a partial last round, or the round
+    robin fallback): dK and dV on sampled keys, dQ on sampled rows, of four
+    heads, against the oracle's row-chunked backward."""
+    _say(f"key-block walk ({B},{H},{N},{d}) causal={causal}")
+    x = make_inputs(B, H, N, d, seed=7 * N + d, with_dout=True)
+    scale = default_scale(d)
+    (q, k, v), o, lse = _run_fwd(x, causal, scale)
+    dq, dk, dv = flash_attn_bwd(to_device(x["do"]), q, k, v, o, lse, causal=causal,
+                                softmax_scale=scale)
+    torch.cuda.synchronize()
+    dq64, dk64, dv64 = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+    rng = np.random.default_rng(N + H)
+    idx = np.unique(np.concatenate([[0, 63, 64, 127, 128, N - 1], rng.choice(N, 18, replace=False)]))
+    BH = B * H
+    for bh in sorted({0, BH - 1, int(rng.integers(BH)), int(rng.integers(BH))}):
+        b, h = divmod(bh, H)
+        xs = {n: x[n][b, h] for n in ("q", "k", "v", "do")}
+        dQ, dK, dV = oracle.attention_backward_sampled(xs["q"], xs["k"], xs["v"], xs["do"], scale,
+                                                       causal, idx, idx)
+        check_grad(dq64[b, h, idx], dQ, f"dQ head {bh}")
+        check_grad(dk64[b, h, idx], dK, f"dK head {bh}")
+        check_grad(dv64[b, h, idx], dV, f"dV head {bh}")
