@@ -22,7 +22,6 @@
 //                (batch, head, 128-key block) items: dK, dV
 //   fa_bwd_q     one workgroup per (batch, head, 128-query block): dQ
 #include <algorithm>
-#include <atomic>
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -131,26 +130,6 @@ struct KvSmem {
   uint16_t* dout[2];
   float* vec[2];
   uint8_t* drop;  // dropout bytes, 1 KiB per wave (DROP only)
-};
-
-// The items (head, key block) of the persistent key-block pass: round r of
-// workgroup b takes item(r).  With the item count and the grid both multiples
-// of 8, workgroup b stays on the XCD of its items (b mod 8, as consecutive
-// workgroups are placed round robin over the 8 XCDs) and walks that XCD's
-// list in snake order (forward in even rounds, backward in odd ones), which
-// pairs the heavy early causal key blocks with light late ones; otherwise
-// round robin over all items.
-struct ItemWalk {
-  int b, G, total;
-  __device__ __forceinline__ int item(int r) const {
-    if (((total | G) & 7) == 0) {
-      const int g = G >> 3, c = b >> 3;
-      const int j = r * g + ((r & 1) ? g - 1 - c : c);
-      return j < (total >> 3) ? 8 * j + (b & 7) : -1;
-    }
-    const int L = b + r * G;
-    return L < total ? L : -1;
-  }
 };
 
 // One workgroup of the key-block pass (8 waves, 16 keys each).  S = Q K^T,
@@ -731,27 +710,11 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 template <int D, bool CAUSAL, bool DROP = false>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t stream) {
   using C = KvCfg<D>;
-  const int64_t items = (int64_t)((a.N + C::BCK - 1) / C::BCK) * a.BH;
-  // one workgroup per CU (the kernel's registers allow no more), a multiple
-  // of 8 so that each stays on the XCD of its items; all items if fewer
-  const int cus = cu_count();
-  int64_t grid = cus > 0 ? std::min<int64_t>(items, cus) : items;
-  if (grid >= 8) grid &= ~int64_t(7);
+  // one workgroup per CU: the kernel's registers allow no more
+  const int64_t grid = persistent_grid((int64_t)((a.N + C::BCK - 1) / C::BCK) * a.BH);
   hipLaunchKernelGGL((fa_bwd_kv_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, a);
   return hipGetLastError();

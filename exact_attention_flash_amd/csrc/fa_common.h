@@ -106,6 +106,26 @@ __device__ __forceinline__ void xcd_head_block(int wg, int total, int BH, int nb
   }
 }
 
+// The items (head, block) of a persistent kernel: round r of workgroup b
+// takes item(r), an index in the run order of xcd_head_block.  With the item
+// count and the grid both multiples of 8, workgroup b stays on the XCD of its
+// items (b mod 8, as consecutive workgroups are placed round robin over the
+// 8 XCDs) and walks that XCD's list in snake order (forward in even rounds,
+// backward in odd ones), which pairs the heavy early causal blocks with light
+// late ones; otherwise round robin over all items.
+struct ItemWalk {
+  int b, G, total;
+  __device__ __forceinline__ int item(int r) const {
+    if (((total | G) & 7) == 0) {
+      const int g = G >> 3, c = b >> 3;
+      const int j = r * g + ((r & 1) ? g - 1 - c : c);
+      return j < (total >> 3) ? 8 * j + (b & 7) : -1;
+    }
+    const int L = b + r * G;
+    return L < total ? L : -1;
+  }
+};
+
 // Heads per group in xcd_head_block.  Measured on causal B=4 H=16 N=4096
 // d=128 (forward + both backward passes): 4 heads per group beat 1 (which
 // ends every group with a long tail) by 8% and 2 by 3%; 8 was within noise

@@ -142,6 +142,7 @@ struct FwdWave {
   int bh;
   const uint16_t* Kh;
   const uint16_t* Vh;
+  const uint16_t* Qh;
   int w, grp, lane, c32, g, N, qw0, qrow;
   int t0;       // first key tile of this workgroup's key range
   int nt, ntw;  // tiles in the range; of those, tiles this wave sees (causal)
@@ -285,6 +286,69 @@ struct FwdWave {
     l_part += rs;
   }
 
+  // Per-item fields for query block qb of head bh and key range `split` of
+  // `splits`, with a fresh running max and sum.
+  __device__ __forceinline__ void begin_item(const FwdArgs& a, int bh_, int qb, int split,
+                                             int splits) {
+    bh = bh_;
+    const int64_t hoff = (int64_t)bh * N * D;
+    Kh = a.k + hoff;
+    Vh = a.v + hoff;
+    Qh = a.q + hoff;
+    const int q0 = qb * C::BR;
+    qw0 = q0 + (2 * (w & 3) + grp) * C::QW;
+    qrow = qw0 + c32;  // the query this lane owns
+    // key tiles the block sees, then this workgroup's range of them
+    int nt_all = (N + BC - 1) / BC;
+    if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + BC - 1) / BC);
+    t0 = split * nt_all / splits;
+    const int t1 = (split + 1) * nt_all / splits;
+    nt = t1 - t0;
+    const int ntw_all = CAUSAL ? min(nt_all, (qw0 + C::QW + BC - 1) / BC) : nt_all;
+    ntw = max(0, min(nt, ntw_all - t0));
+    m_run = -INFINITY;
+    l_part = 0.f;
+  }
+
+  // K tiles 0 and 1 and V tile 0 of the item's range, before its first
+  // period (an empty range, possible only for a split, copies nothing), and
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
+  __device__ __forceinline__ void issue_prologue(const FwdArgs& a) {
+    if (nt > 0) {
+      cp.template issue<true>(Kh, sm.k[0], t0 * BC, N, w, lane);
+      if (nt > 1) cp.template issue<true>(Kh, sm.k[1], (t0 + 1) * BC, N, w, lane);
+      cp.template issue<false>(Vh, sm.v[0], t0 * BC, N, w, lane);
+    }
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      qf[kc] = qrow < N ? load_global<bf16x8>(Qh + (int64_t)qrow * D + kc * 16 + g * 8)
+                        : zero_bf16x8();
+  }
+
+  __device__ __forceinline__ void zero_o() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+  }
+
+  // Epilogue of the item with head bh_ whose lane row is row: one division
+  // by l (and the dropout rescale), LSE = (m + log2 l) ln 2.
+  __device__ __forceinline__ void store_out(const FwdArgs& a, int bh_, int row, float l,
+                                            float m) const {
+    if (row >= N) return;
+    const float inv = DROP ? drop.scale / l : 1.f / l;
+    uint16_t* Orow = a.o + (int64_t)bh_ * N * D + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 val;
+        val.x = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+        val.y = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * g) = val;
+      }
+    if (g == 0) a.lse[(int64_t)bh_ * N + row] = (m + log2_fast(l)) * kLn2;
+  }
+
   // One period (two barrier-separated slots) of a wave of group GRP.  R = t
   // mod 3 names the buffers: K tile t in K buffer R, V tile t - 1 in V buffer
   // (R + 2) mod 3.  The period also starts the copies of K tile t + 2 (into
@@ -354,22 +418,10 @@ fa_fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
 
-  // Workgroup -> (head, query block[, key range]): heads grouped per XCD,
-  // heaviest (last) causal query blocks first.
-  const int split = SPLIT ? (int)(blockIdx.x % (unsigned)a.splits) : 0;
-  const int wg = SPLIT ? (int)(blockIdx.x / (unsigned)a.splits) : (int)blockIdx.x;
-  const int total = SPLIT ? (int)(gridDim.x / (unsigned)a.splits) : (int)gridDim.x;
-  int bh, qb;
-  xcd_head_block<kHeadsPerGroup>(wg, total, a.BH, nqb, bh, qb);
-  if (CAUSAL) qb = nqb - 1 - qb;
-
-  const int64_t hoff = (int64_t)bh * N * D;
+  // per-lane constants, the same for every item
   FwdWave<D, CAUSAL, DROP> f;
   f.sm = FwdSmem{{k0s, k1s, k2s}, {v0s, v1s, v2s}};
   f.drop = a.drop;
-  f.bh = bh;
-  f.Kh = a.k + hoff;
-  f.Vh = a.v + hoff;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   // Waves w and w + 4 run on the same SIMD: they form a ping-pong pair and
   // take adjacent 32-row chunks, so the pair's causal work is balanced.
@@ -378,50 +430,31 @@ fa_fwd_kernel(FwdArgs a) {
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
   f.N = N;
-  const int q0 = qb * C::BR;
-  f.qw0 = q0 + (2 * (f.w & 3) + f.grp) * C::QW;
-  f.qrow = f.qw0 + f.c32;  // the query this lane owns
-  // key tiles the block sees, then this workgroup's range of them
-  int nt_all = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + C::BC - 1) / C::BC);
-  f.t0 = SPLIT ? split * nt_all / a.splits : 0;
-  const int t1 = SPLIT ? (split + 1) * nt_all / a.splits : nt_all;
-  f.nt = t1 - f.t0;
-  const int ntw_all = CAUSAL ? min(nt_all, (f.qw0 + C::QW + C::BC - 1) / C::BC) : nt_all;
-  f.ntw = max(0, min(f.nt, ntw_all - f.t0));
   f.sl2 = a.scale_log2;
-  f.m_run = -INFINITY;
-  f.l_part = 0.f;
   f.trv = TrLane<D>(f.lane);
   f.kbase = f.c32 * D;
   f.ku = f.g ^ chunk_swizzle<D>(f.c32);
   f.cp.init(f.w, f.lane);
 
-  // K tiles 0 and 1 and V tile 0 of the range before the first period (an
-  // empty range, possible only for a split, skips the loop altogether).
-  if (f.nt > 0) {
-    f.cp.template issue<true>(f.Kh, k0s, f.t0 * C::BC, N, f.w, f.lane);
-    if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, (f.t0 + 1) * C::BC, N, f.w, f.lane);
-    f.cp.template issue<false>(f.Vh, v0s, f.t0 * C::BC, N, f.w, f.lane);
-  }
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
-  const uint16_t* Qh = a.q + hoff;
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc)
-    f.qf[kc] = f.qrow < N ? load_global<bf16x8>(Qh + (int64_t)f.qrow * D + kc * 16 + f.g * 8)
-                          : zero_bf16x8();
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) f.oacc[db] = zero16();
-  wait_vmem();
-  block_barrier();
-
-  if (f.nt > 0) {
-    if (f.grp == 0) f.template run<0>();
-    else f.template run<1>();
-  }
-
-  const float l = sum_halves(f.l_part);
-  if (SPLIT) {
+  if constexpr (SPLIT) {
+    // Workgroup -> (head, query block, key range): heads grouped per XCD,
+    // heaviest (last) causal query blocks first.
+    const int split = (int)(blockIdx.x % (unsigned)a.splits);
+    const int total = (int)(gridDim.x / (unsigned)a.splits);
+    int bh, qb;
+    xcd_head_block<kHeadsPerGroup>((int)(blockIdx.x / (unsigned)a.splits), total, a.BH, nqb, bh,
+                                   qb);
+    if (CAUSAL) qb = nqb - 1 - qb;
+    f.begin_item(a, bh, qb, split, a.splits);
+    f.issue_prologue(a);
+    f.zero_o();
+    wait_vmem();
+    block_barrier();
+    if (f.nt > 0) {
+      if (f.grp == 0) f.template run<0>();
+      else f.template run<1>();
+    }
+    const float l = sum_halves(f.l_part);
     // the range's partials, relative to its own running max
     if (f.qrow < N) {
       const int64_t row = ((int64_t)split * a.BH + bh) * N + f.qrow;
@@ -440,22 +473,53 @@ fa_fwd_kernel(FwdArgs a) {
         a.lpart[row] = l;
       }
     }
-    return;
-  }
-  // Epilogue: one division by l (and the dropout rescale), LSE = (m + log2 l) ln 2.
-  if (f.qrow < N) {
-    const float inv = DROP ? a.drop.scale / l : 1.f / l;
-    uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
+  } else {
+    // Persistent: the grid walks the (head, query block) items in run order
+    // (heads grouped per XCD, heaviest causal query blocks first).  After an
+    // item's last period every buffer is free, so the next item's first
+    // copies and Q loads are issued before this item's epilogue and overlap
+    // it.
+    const ItemWalk walk{(int)blockIdx.x, (int)gridDim.x, a.BH * nqb};
+    int bh, qb;
+    xcd_head_block<kHeadsPerGroup>(walk.item(0), walk.total, a.BH, nqb, bh, qb);
+    f.begin_item(a, bh, CAUSAL ? nqb - 1 - qb : qb, 0, 1);
+    f.issue_prologue(a);
+    f.zero_o();
+    wait_vmem();
+    block_barrier();
+    for (int r = 1;; ++r) {
+      // fresh copies of the per-lane constants each item, so that nothing
+      // derived from them is hoisted out of the item loop and held across it
+      f.kbase = opaque(f.kbase);
+      f.ku = opaque(f.ku);
+      f.trv = f.trv.fresh();
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 val;
-        val.x = pack2(f.oacc[db][4 * r4 + 0] * inv, f.oacc[db][4 * r4 + 1] * inv);
-        val.y = pack2(f.oacc[db][4 * r4 + 2] * inv, f.oacc[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * f.g) = val;
+      for (int t = 0; t < C::COPIES; ++t) {
+        f.cp.koff[t] = (uint32_t)opaque((int)f.cp.koff[t]);
+        f.cp.voff[t] = (uint32_t)opaque((int)f.cp.voff[t]);
       }
-    if (f.g == 0) a.lse[(int64_t)bh * N + f.qrow] = (f.m_run + log2_fast(l)) * kLn2;
+      if (f.grp == 0) f.template run<0>();
+      else f.template run<1>();
+      const float l = sum_halves(f.l_part);
+      const float m = f.m_run;
+      const int cur_bh = f.bh, cur_row = f.qrow;
+      const int L = walk.item(r);
+      if (L >= 0) {
+        xcd_head_block<kHeadsPerGroup>(L, walk.total, a.BH, nqb, bh, qb);
+        f.begin_item(a, bh, CAUSAL ? nqb - 1 - qb : qb, 0, 1);
+        f.issue_prologue(a);
+      }
+      f.store_out(a, cur_bh, cur_row, l, m);
+      if (L < 0) break;
+      f.zero_o();
+      // the previous item's scores and probabilities are dead: say so
+#pragma unroll
+      for (int sb = 0; sb < C::BC / 32; ++sb) f.s[sb] = zero16();
+#pragma unroll
+      for (int kc2 = 0; kc2 < C::BC / 16; ++kc2) f.pb[kc2] = zero_bf16x8();
+      wait_vmem();
+      block_barrier();
+    }
   }
 }
 
@@ -499,7 +563,8 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int64_t nqb = (a.N + C::BR - 1) / C::BR;
-  const int64_t grid = nqb * a.BH;
+  // persistent: one workgroup per CU (the kernel's registers allow no more)
+  const int64_t grid = persistent_grid(nqb * a.BH);
   hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, a);
   return hipGetLastError();
@@ -530,7 +595,7 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_dropout_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int64_t nqb = (a.N + C::BR - 1) / C::BR;
-  const int64_t grid = nqb * a.BH;
+  const int64_t grid = persistent_grid(nqb * a.BH);
   hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false, true>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, a);
   return hipGetLastError();

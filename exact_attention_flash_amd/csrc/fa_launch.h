@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace fa {
 
 // Dropout on the attention probabilities (inactive unless a kernel is
@@ -94,6 +97,28 @@ struct BwdArgs {
   float scale_log2;   // softmax_scale * log2(e)
   DropArgs drop;
 };
+
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Grid of a persistent kernel over `items` work items with one workgroup per
+// CU: at most one per CU and never more than the items, a multiple of 8 when
+// at least 8 (so that each workgroup stays on the XCD of its items).
+inline int64_t persistent_grid(int64_t items) {
+  const int cus = cu_count();
+  int64_t grid = cus > 0 ? std::min<int64_t>(items, cus) : items;
+  if (grid >= 8) grid &= ~int64_t(7);
+  return grid;
+}
 
 // Enqueue the forward kernel for head dim d (64 or 128).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
