@@ -32,33 +32,47 @@ namespace fa {
 // Row pass over [B*H, Npad] rows (Npad = N rounded up to the query block):
 // D = rowsum(dO o O) and LSE * log2(e) for real rows, D = 0 and +inf for the
 // padding rows (so a padded query gets P = 0 in the key-block pass).
+// Each thread takes 16 bytes of PRE_ROWS rows, RPB rows apart, and issues
+// all of its loads before any arithmetic.
+constexpr int PRE_ROWS = 4;
+
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;       // threads per row (16-byte chunks)
-  constexpr int RPB = 256 / TPR;   // rows per workgroup
+  constexpr int RPB = 256 / TPR;   // rows per pass of the workgroup
   const int tid = threadIdx.x;
-  const int64_t rr = (int64_t)blockIdx.x * RPB + tid / TPR;
   const int ch = tid % TPR;
   const int64_t rows = (int64_t)a.BH * a.Npad;
-  const int64_t bh = rr / a.Npad;
-  const int q = (int)(rr - bh * a.Npad);
-  const bool real = rr < rows && q < a.N;
-  const int64_t row = bh * a.N + q;  // row of the [B*H, N] tensors
-  float acc = 0.f;
-  if (real) {
-    const u32x4 o = load_global<u32x4>(a.o + row * D + ch * 8);
-    const u32x4 d = load_global<u32x4>(a.dout + row * D + ch * 8);
+  const int64_t r0 = (int64_t)blockIdx.x * RPB * PRE_ROWS + tid / TPR;
+  u32x4 o[PRE_ROWS], d[PRE_ROWS];
+  float lv[PRE_ROWS];
+  bool real[PRE_ROWS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(bf16_to_f32((uint16_t)(o[j] & 0xffffu)), bf16_to_f32((uint16_t)(d[j] & 0xffffu)), acc);
-      acc = fmaf(bf16_to_f32((uint16_t)(o[j] >> 16)), bf16_to_f32((uint16_t)(d[j] >> 16)), acc);
-    }
+  for (int k = 0; k < PRE_ROWS; ++k) {
+    const int64_t rr = r0 + k * RPB;
+    const int64_t bh = rr / a.Npad;
+    const int q = (int)(rr - bh * a.Npad);
+    real[k] = rr < rows && q < a.N;
+    const int64_t row = bh * a.N + q;  // row of the [B*H, N] tensors
+    o[k] = real[k] ? load_global<u32x4>(a.o + row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    d[k] = real[k] ? load_global<u32x4>(a.dout + row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    lv[k] = real[k] && ch == 0 ? a.lse[row] : 0.f;
   }
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (rr < rows && ch == 0) {
-    a.delta[rr] = acc;
-    a.lse2[rr] = real ? a.lse[row] * kLog2e : INFINITY;
+  for (int k = 0; k < PRE_ROWS; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(bf16_to_f32((uint16_t)(o[k][j] & 0xffffu)), bf16_to_f32((uint16_t)(d[k][j] & 0xffffu)), acc);
+      acc = fmaf(bf16_to_f32((uint16_t)(o[k][j] >> 16)), bf16_to_f32((uint16_t)(d[k][j] >> 16)), acc);
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    const int64_t rr = r0 + k * RPB;
+    if (rr < rows && ch == 0) {
+      a.delta[rr] = acc;
+      a.lse2[rr] = real[k] ? lv[k] * kLog2e : INFINITY;
+    }
   }
 }
 
@@ -704,8 +718,8 @@ fa_bwd_q_kernel(BwdArgs a) {
 template <int D>
 static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Npad;
-  const int64_t rpb = 256 / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
+  const int64_t rpw = 256 / (D / 8) * PRE_ROWS;  // rows per workgroup
+  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }
