@@ -412,7 +412,9 @@ def test_bwd_key_block_walk(B, H, N, d, causal):
     """Backward where the persistent key-block pass gives workgroups several
     items (and an odd number of rounds, a partial last round, or the round
     robin fallback): dK and dV on sampled keys, dQ on sampled rows, of four
-    heads, against the oracle's row-chunked backward."""
+    heads, against the oracle's row-chunked backward; O and LSE of the
+    persistent forward (several query blocks per workgroup on the largest
+    shape) on the same rows."""
     _say(f"key-block walk ({B},{H},{N},{d}) causal={causal}")
     x = make_inputs(B, H, N, d, seed=7 * N + d, with_dout=True)
     scale = default_scale(d)
@@ -421,12 +423,16 @@ def test_bwd_key_block_walk(B, H, N, d, causal):
                                 softmax_scale=scale)
     torch.cuda.synchronize()
     dq64, dk64, dv64 = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+    o64, lse64 = bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(N + H)
     idx = np.unique(np.concatenate([[0, 63, 64, 127, 128, N - 1], rng.choice(N, 18, replace=False)]))
     BH = B * H
     for bh in sorted({0, BH - 1, int(rng.integers(BH)), int(rng.integers(BH))}):
         b, h = divmod(bh, H)
         xs = {n: x[n][b, h] for n in ("q", "k", "v", "do")}
+        Or, Lr = oracle.attention_forward_rows(xs["q"], xs["k"], xs["v"], scale, causal, idx)
+        check_o(o64[b, h, idx], Or, f"O head {bh}")
+        check_lse(lse64[b, h, idx], Lr, f"LSE head {bh}")
         dQ, dK, dV = oracle.attention_backward_sampled(xs["q"], xs["k"], xs["v"], xs["do"], scale,
                                                        causal, idx, idx)
         check_grad(dq64[b, h, idx], dQ, f"dQ head {bh}")
