@@ -347,33 +347,18 @@ fa_fwd_fp8_kernel(Fp8FwdArgs a) {
   const int tid = threadIdx.x;
   const int N = a.N;
   const int nqb = (N + C::BR - 1) / C::BR;
-  int bh, qb;
-  xcd_head_block<kHeadsPerGroup>((int)blockIdx.x, (int)gridDim.x, a.BH, nqb, bh, qb);
-  if (CAUSAL) qb = nqb - 1 - qb;
 
-  const int64_t hoff = (int64_t)bh * N * D;
+  // per-lane constants, the same for every item
   Fp8Wave<D, CAUSAL> f;
   f.sm = Fp8Smem{{k0s, k1s, k2s}, {v0s, v1s, v2s}};
-  f.Kh = a.k + hoff;
-  f.Vh = a.v + hoff;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   f.grp = f.w >> 2;
   f.lane = tid & 63;
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
   f.N = N;
-  const int q0 = qb * C::BR;
-  f.qw0 = q0 + (2 * (f.w & 3) + f.grp) * C::QW;
-  f.qrow = f.qw0 + f.c32;
-  int nt_all = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + C::BC - 1) / C::BC);
   f.t0 = 0;
-  f.nt = nt_all;
-  f.ntw = CAUSAL ? min(nt_all, (f.qw0 + C::QW + C::BC - 1) / C::BC) : nt_all;
-  asm volatile("" : "+s"(f.ntw));  // keep the per-tile tests: knowing ntw == nt hoists more
   f.sl2 = a.scale_log2;
-  f.m_run = -INFINITY;
-  f.l_part = 0.f;
   f.kb = f.c32 * D + 16 * ((2 * f.g) ^ fp8_k_swizzle<D>(f.c32));
   {
     // lane 16 u + 2 jj + h of the transposed V reads: group u = (g, column
@@ -384,34 +369,43 @@ fa_fwd_fp8_kernel(Fp8FwdArgs a) {
   }
   f.cp.init(f.w, f.lane);
 
-  f.cp.template issue<true>(f.Kh, k0s, 0, N, f.w, f.lane);
-  if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, C::BC, N, f.w, f.lane);
-  f.cp.template issue<false>(f.Vh, v0s, 0, N, f.w, f.lane);
-  const uint8_t* Qh = a.q + hoff;
+  // Item (head bh, query block qb): its fields with a fresh running max and
+  // sum, the copies of K tiles 0 and 1 and V tile 0, and Q into registers.
+  auto begin = [&](int bh, int qb) {
+    const int64_t hoff = (int64_t)bh * N * D;
+    f.Kh = a.k + hoff;
+    f.Vh = a.v + hoff;
+    const int q0 = qb * C::BR;
+    f.qw0 = q0 + (2 * (f.w & 3) + f.grp) * C::QW;
+    f.qrow = f.qw0 + f.c32;
+    int nt_all = (N + C::BC - 1) / C::BC;
+    if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + C::BC - 1) / C::BC);
+    f.nt = nt_all;
+    f.ntw = CAUSAL ? min(nt_all, (f.qw0 + C::QW + C::BC - 1) / C::BC) : nt_all;
+    asm volatile("" : "+s"(f.ntw));  // keep the per-tile tests: knowing ntw == nt hoists more
+    f.m_run = -INFINITY;
+    f.l_part = 0.f;
+    f.cp.template issue<true>(f.Kh, k0s, 0, N, f.w, f.lane);
+    if (f.nt > 1) f.cp.template issue<true>(f.Kh, k1s, C::BC, N, f.w, f.lane);
+    f.cp.template issue<false>(f.Vh, v0s, 0, N, f.w, f.lane);
+    const uint8_t* Qh = a.q + hoff;
 #pragma unroll
-  for (int kc = 0; kc < C::KS; ++kc) {
-    if (f.qrow < N) {
-      const uint8_t* src = Qh + (int64_t)f.qrow * D + 64 * kc + 32 * f.g;
-      f.qf[kc] = join8(load_global<i32x4>(src), load_global<i32x4>(src + 16));
-    } else {
+    for (int kc = 0; kc < C::KS; ++kc) {
+      if (f.qrow < N) {
+        const uint8_t* src = Qh + (int64_t)f.qrow * D + 64 * kc + 32 * f.g;
+        f.qf[kc] = join8(load_global<i32x4>(src), load_global<i32x4>(src + 16));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f.qf[kc][e] = 0;
+        for (int e = 0; e < 8; ++e) f.qf[kc][e] = 0;
+      }
     }
-  }
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) f.oacc[db] = zero16();
-  wait_vmem();
-  block_barrier();
-
-  if (f.grp == 0) f.template run<0>();
-  else f.template run<1>();
-
+  };
   // O = descale_v * acc / l; LSE = (m - kP + log2 l) ln 2 (both acc and l
   // carry the factor 2^kP).
-  const float l = sum_halves(f.l_part);
-  if (f.qrow < N) {
+  auto finish = [&](int bh, int row, float l, float m) {
+    if (row >= N) return;
     const float inv = a.descale_v / l;
-    uint16_t* Orow = a.o + hoff + (int64_t)f.qrow * D;
+    uint16_t* Orow = a.o + (int64_t)bh * N * D + (int64_t)row * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -421,8 +415,53 @@ fa_fwd_fp8_kernel(Fp8FwdArgs a) {
         val.y = pack2(f.oacc[db][4 * r4 + 2] * inv, f.oacc[db][4 * r4 + 3] * inv);
         *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * r4 + 4 * f.g) = val;
       }
-    if (f.g == 0)
-      a.lse[(int64_t)bh * N + f.qrow] = (f.m_run - kFp8PExp + log2_fast(l)) * kLn2;
+    if (f.g == 0) a.lse[(int64_t)bh * N + row] = (m - kFp8PExp + log2_fast(l)) * kLn2;
+  };
+
+  // Persistent: the grid walks the (head, query block) items in run order
+  // (heads grouped per XCD, heaviest causal query blocks first); the next
+  // item's first copies and Q loads overlap the current item's epilogue.
+  const ItemWalk walk{(int)blockIdx.x, (int)gridDim.x, a.BH * nqb};
+  int bh, qb;
+  xcd_head_block<kHeadsPerGroup>(walk.item(0), walk.total, a.BH, nqb, bh, qb);
+  begin(bh, CAUSAL ? nqb - 1 - qb : qb);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) f.oacc[db] = zero16();
+  wait_vmem();
+  block_barrier();
+  for (int r = 1;; ++r) {
+    // fresh copies of the per-lane constants each item, so that nothing
+    // derived from them is hoisted out of the item loop and held across it
+    f.kb = opaque(f.kb);
+    f.vb = opaque(f.vb);
+#pragma unroll
+    for (int t = 0; t < C::COPIES; ++t) {
+      f.cp.koff[t] = (uint32_t)opaque((int)f.cp.koff[t]);
+      f.cp.voff[t] = (uint32_t)opaque((int)f.cp.voff[t]);
+    }
+    if (f.grp == 0) f.template run<0>();
+    else f.template run<1>();
+    const float l = sum_halves(f.l_part);
+    const float m = f.m_run;
+    const int cur_bh = bh, cur_row = f.qrow;
+    const int L = walk.item(r);
+    if (L >= 0) {
+      xcd_head_block<kHeadsPerGroup>(L, walk.total, a.BH, nqb, bh, qb);
+      begin(bh, CAUSAL ? nqb - 1 - qb : qb);
+    }
+    finish(cur_bh, cur_row, l, m);
+    if (L < 0) break;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) f.oacc[db] = zero16();
+    // the previous item's scores and probabilities are dead: say so
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) f.s[sb] = zero16();
+#pragma unroll
+    for (int ps = 0; ps < C::PS; ++ps)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f.pb[ps][e] = 0;
+    wait_vmem();
+    block_barrier();
   }
 }
 
@@ -430,7 +469,8 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_fp8_t(const Fp8FwdArgs& a, hipStream_t stream) {
   using C = Fp8Cfg<D>;
   const int64_t nqb = (a.N + C::BR - 1) / C::BR;
-  const int64_t grid = nqb * a.BH;
+  // persistent: one workgroup per CU (the kernel's registers allow no more)
+  const int64_t grid = persistent_grid(nqb * a.BH);
   hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, a);
   return hipGetLastError();
