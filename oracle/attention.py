@@ -93,6 +93,21 @@ def _heads(q, k, v):
     return q.shape
 
 
+def _heads_qkv(q, k, v, causal: bool):
+    """Shapes of a forward whose queries and keys may differ in number:
+    q [B, H, N_q, d], k and v [B, H, N_kv, d].  The decode step of the CMU
+    notes (section "生成式 LLM 推理") attends from one new query to every
+    cached key and value, and the apxml example's interface gives queries
+    and keys their own sequence lengths.  The causal mask (key j visible to
+    query i iff j <= i) is only taken for equal lengths."""
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, N_q, d] and k, v [B, H, N_kv, d]")
+    if causal and q.shape[2] != k.shape[2]:
+        raise ValueError("the causal mask needs as many queries as keys")
+    return q.shape
+
+
 def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
     """P = softmax(scale * Q K^T (masked)) for every head, ``[B, H, N, N]``."""
     q, k = _f64(q), _f64(k)
@@ -109,10 +124,12 @@ def attention_forward(q, k, v, scale: float, causal: bool,
     """O = softmax(scale * Q K^T) V and LSE, both float64.
 
     Inputs are ``[B, H, N, d]`` arrays (uint16 bf16 bit patterns are widened
-    exactly).  Returns ``O [B, H, N, d]`` and ``LSE [B, H, N]`` with
-    LSE_i = m_i + ln l_i.  ``row_chunk`` bounds the rows of S held at once;
-    every chunk holds complete rows, and rows are independent, so chunking
-    changes nothing in the arithmetic.
+    exactly); without the causal mask, k and v may hold another number of
+    rows than q (``[B, H, N_kv, d]``, a decode step).  Returns
+    ``O [B, H, N, d]`` and ``LSE [B, H, N]`` with LSE_i = m_i + ln l_i.
+    ``row_chunk`` bounds the rows of S held at once; every chunk holds
+    complete rows, and rows are independent, so chunking changes nothing in
+    the arithmetic.
 
     Follows the apxml manual fallback (scores, causal bias, row softmax, @ V)
     and the CMU notes' steps 2-5; LSE follows the reading that the single
@@ -121,7 +138,7 @@ def attention_forward(q, k, v, scale: float, causal: bool,
     per-row sum of exponentials.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, N, d = _heads(q, k, v)
+    B, H, N, d = _heads_qkv(q, k, v, causal)
     R = N if row_chunk is None else max(1, int(row_chunk))
     O = np.empty((B, H, N, d))
     LSE = np.empty((B, H, N))
@@ -143,6 +160,8 @@ def attention_forward_rows(q, k, v, scale: float, causal: bool, rows):
     the whole-head result restricted to those rows.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
+    if causal and q.shape[0] != k.shape[0]:
+        raise ValueError("the causal mask needs as many queries as keys")
     rows = np.asarray(rows, dtype=np.int64)
     s = scores(q[rows], k, scale, causal, rows=rows)
     m, ell, p = softmax_rows(s)

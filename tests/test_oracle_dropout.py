@@ -15,6 +15,10 @@ counter layout, a mask missing from dP) and shows these pins catch them.
 """
 
 import math
+import os
+import shutil
+import subprocess
+import tempfile
 
 import numpy as np
 import pytest
@@ -52,6 +56,51 @@ def test_philox4x64_matches_numpy(counter, key):
         v = (c[0] | c[1] << 64 | c[2] << 128 | c[3] << 192) + 1
         c = [(v >> (64 * i)) & (2**64 - 1) for i in range(4)]
         assert od.philox(c, key, width=64) == blocks[b]
+
+
+ROCRAND_HEADER = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+ROCRAND_PROG = os.path.join(os.path.dirname(os.path.abspath(__file__)), "philox_rocrand.cpp")
+
+
+def rocrand_philox4x32(blocks):
+    """Philox4x32-10 output words of each (counter, key) in ``blocks`` from
+    rocRAND's header-only engine, compiled for the host with g++ on first use
+    (a library implementation written independently of the oracle)."""
+    if not os.path.exists(ROCRAND_HEADER) or shutil.which("g++") is None:
+        pytest.skip("rocRAND headers or g++ not available")
+    exe = os.path.join(tempfile.gettempdir(), f"philox_rocrand_{os.getpid()}")
+    if not os.path.exists(exe):
+        subprocess.run(["g++", "-std=c++17", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        ROCRAND_PROG, "-o", exe], check=True, capture_output=True)
+    text = "".join(" ".join(str(int(x)) for x in (*c, *k)) + "\n" for c, k in blocks)
+    out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+    return [[int(w) for w in line.split()] for line in out.strip().splitlines()]
+
+
+def _philox32_cases():
+    rng = np.random.default_rng(321)
+    cases = [([0, 0, 0, 0], [0, 0]), ([1, 2, 3, 4], [5, 6]),
+             ([2**32 - 1] * 4, [2**32 - 1, 2**32 - 1]),
+             # the layout the kernels use: (key group, query, head, offset)
+             ([255, 4095, 63, 0], [0x5EED, 0]), ([3, 17, 5, 9], [0xDEADBEEF, 0x01234567])]
+    for _ in range(60):
+        cases.append(([int(x) for x in rng.integers(0, 2**32, 4)],
+                      [int(x) for x in rng.integers(0, 2**32, 2)]))
+    return cases
+
+
+def test_philox4x32_matches_rocrand():
+    """The width-32 instance (multipliers, Weyl increments, round structure,
+    word order) against rocRAND's philox4x32_10 engine, for the scalar and
+    the vectorised oracle paths."""
+    cases = _philox32_cases()
+    ref = rocrand_philox4x32(cases)
+    assert len(ref) == len(cases)
+    for (c, k), r in zip(cases, ref):
+        assert od.philox(c, k, width=32) == r, (c, k)
+    for (cc, k), r in zip(cases[:8], ref[:8]):
+        got = od.philox4x32_10_array(cc[0], cc[1], cc[2], cc[3], k[0], k[1])
+        assert [int(x) for x in got] == r
 
 
 def test_weyl_increments_closed_form():

@@ -70,6 +70,57 @@ def test_torch_sdpa_fp64_cpu(causal):
     np.testing.assert_allclose(O, ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- queries != keys (decode)
+def _brute_head_lengths(q, k, v, scale):
+    """Full attention of len(q) queries over len(k) keys, per element in pure
+    Python (math.fsum), no max subtraction."""
+    d = len(q[0])
+    O, lse = [], []
+    for qi in q:
+        w = [math.exp(scale * math.fsum(qi[t] * kj[t] for t in range(d))) for kj in k]
+        den = math.fsum(w)
+        O.append([math.fsum(w[j] * v[j][c] for j in range(len(k))) / den
+                  for c in range(len(v[0]))])
+        lse.append(math.log(den))
+    return np.array(O), np.array(lse)
+
+
+@pytest.mark.parametrize("Nq,Nk,d", [(1, 1, 3), (1, 9, 4), (3, 7, 2), (6, 2, 3)])
+def test_unequal_lengths_brute_force(Nq, Nk, d):
+    """A decode step (one query, or a few, against every cached key) and the
+    reverse: against per-element sums."""
+    q, k, v = _rand(1, 2, Nq, d), _rand(1, 2, Nk, d), _rand(1, 2, Nk, d)
+    O, L = oracle.attention_forward(q, k, v, 0.6, False)
+    assert O.shape == (1, 2, Nq, d) and L.shape == (1, 2, Nq)
+    for h in range(2):
+        Ob, Lb = _brute_head_lengths(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), 0.6)
+        np.testing.assert_allclose(O[0, h], Ob, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(L[0, h], Lb, rtol=1e-12, atol=1e-13)
+
+
+def test_unequal_lengths_torch_sdpa_and_closed_form():
+    """torch's fp64 SDPA with queries and keys of different lengths (the
+    apxml example's interface), and the closed form for Q = 0: every query
+    takes the mean of all N_kv values and LSE = ln N_kv."""
+    B, H, Nq, Nk, d = 2, 3, 5, 41, 16
+    q, k, v = _rand(B, H, Nq, d), _rand(B, H, Nk, d), _rand(B, H, Nk, d)
+    O, _ = oracle.attention_forward(q, k, v, 0.25, False)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.25)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=1e-12, atol=1e-12)
+    O0, L0 = oracle.attention_forward(np.zeros_like(q), k, v, 0.25, False)
+    np.testing.assert_allclose(O0, np.broadcast_to(v.mean(axis=2, keepdims=True), O0.shape),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(L0, np.log(Nk), rtol=1e-15)
+    rows = np.array([4, 0, 2])
+    Or, Lr = oracle.attention_forward_rows(q[1, 2], k[1, 2], v[1, 2], 0.25, False, rows)
+    np.testing.assert_allclose(Or, O[1, 2, rows], rtol=1e-14, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.attention_forward(q, k, v, 0.25, True)   # causal needs equal lengths
+    with pytest.raises(ValueError):
+        oracle.attention_forward(q, k, v[:, :, :-1], 0.25, False)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_scipy_softmax_and_logsumexp(causal):
     N, d = 23, 8
@@ -186,6 +237,22 @@ def test_bf16_bits_are_widened_exactly():
     assert np.array_equal(O_bits, O_f)
     with pytest.raises(TypeError):
         oracle.widen_bf16(np.zeros(3, dtype=np.int16))
+
+
+def test_widen_bf16_matches_torch_on_every_pattern():
+    """All 65536 bf16 bit patterns widen to the value torch's own bfloat16 ->
+    float64 conversion gives (a library routine): same value, same sign of
+    zero, NaN exactly where torch has NaN, infinities included."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns
+        ours = oracle.widen_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert int(nan.sum()) == 2 * 127  # exponent all ones, non-zero mantissa, both signs
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    assert np.isposinf(ours[0x7F80]) and np.isneginf(ours[0xFF80])
 
 
 @pytest.mark.parametrize("causal", [False, True])

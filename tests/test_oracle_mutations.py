@@ -161,7 +161,24 @@ MUTATIONS_FP8 = [
 ]
 
 
+def _keys_cut_to_queries(q, k, scale, causal, row_start=0, rows=None):
+    # a slip that only shows when queries and keys differ in number: the
+    # query count taken as the key count (keys past it masked out)
+    s = _REAL_SCORES(q, k, scale, causal, row_start, rows)
+    s[:, max(1, q.shape[0]):] = -np.inf
+    return s
+
+
+_REAL_SCORES = oa.scores
+
+
+def _pin_unequal_lengths():
+    from tests.test_oracle_forward import test_unequal_lengths_brute_force
+    test_unequal_lengths_brute_force(1, 9, 4)
+
+
 MUTATIONS = [
+    ("scores", _keys_cut_to_queries, _pin_unequal_lengths),
     ("scores", _no_scale_scores, lambda: _pin_torch_sdpa(False)),
     ("scores", _shifted_mask_scores, _pin_causal_row0),
     ("softmax_rows", _no_max_in_lse, _pin_logsumexp),
@@ -414,3 +431,55 @@ def test_sampled_backward_pin_catches_planted_mistake(monkeypatch, name, bad):
     monkeypatch.setattr(oracle, "attention_backward_sampled", bad)
     with pytest.raises(AssertionError):
         _pin_sampled()
+
+
+# ---------------------------------------------------------------- bf16 widening, Philox4x32
+def _widen_byteswapped(bits):
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError(b.dtype)
+    return (b.byteswap().astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _widen_low_half(bits):
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError(b.dtype)
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _pin_widen_torch():
+    from tests.test_oracle_forward import test_widen_bf16_matches_torch_on_every_pattern
+    test_widen_bf16_matches_torch_on_every_pattern()
+
+
+def _philox32_swapped_multiplier(counter, key, width=32, rounds=10):
+    # only the 32-bit multipliers exchanged (numpy's 4x64 pin cannot see this)
+    if width != 32:
+        return _REAL_PHILOX(counter, key, width, rounds)
+    return _philox_swapped_multipliers(counter, key, width, rounds)
+
+
+def _pin_rocrand_philox():
+    from tests.test_oracle_dropout import test_philox4x32_matches_rocrand
+    test_philox4x32_matches_rocrand()
+
+
+MUTATIONS_BITS = [
+    (oa, "widen_bf16", _widen_byteswapped, _pin_widen_torch),
+    (oa, "widen_bf16", _widen_low_half, _pin_widen_torch),
+    (odr, "philox", _philox32_swapped_multiplier, _pin_rocrand_philox),
+    (odr, "philox", _philox_seven_rounds, _pin_rocrand_philox),
+]
+
+
+@pytest.mark.parametrize("mod,target,bad,pin", MUTATIONS_BITS,
+                         ids=[f"{m[2].__name__}-{m[3].__name__}" for m in MUTATIONS_BITS])
+def test_bits_pin_catches_planted_mistake(monkeypatch, mod, target, bad, pin):
+    pin()
+    monkeypatch.setattr(mod, target, bad)
+    if hasattr(oracle, target):
+        monkeypatch.setattr(oracle, target, bad)
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            pin()
