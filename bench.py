@@ -60,6 +60,11 @@ def parse_args():
                          "fwd+bwd and long-context shapes; reported under 'fp8_forward'")
     ap.add_argument("--naive", action="store_true",
                     help="also time the materialise-S forward in bf16 torch ops on the same inputs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing every named workload on its own (reported under "
+                         "'configs', each with the oracle timed on a sample of it)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step split-KV timings (reported under 'decode')")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters); not timed")
@@ -88,26 +93,34 @@ def load_traffic(kernel: str, sha: str):
     return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
 
 
+def host_blas():
+    """(BLAS library description, its thread count) of this process's numpy."""
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = sum(int(p.get("num_threads", 1)) for p in pools) or 1
+        blas = ", ".join(f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                         for p in pools) or "unknown"
+        return blas, threads
+    except Exception:  # pragma: no cover
+        return "unknown", None
+
+
+def cpu_model_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        return "unknown"
+
+
 def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
     """The fp64 oracle on ``n_heads`` whole heads of the step, timed here."""
     import numpy as np
     import oracle
-    blas = "unknown"
-    try:
-        from threadpoolctl import threadpool_info
-        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = sum(int(p.get("num_threads", 1)) for p in pools) or 1
-        if pools:
-            blas = ", ".join(f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
-                             for p in pools)
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
+    blas, blas_threads = host_blas()
+    cores = len(os.sched_getaffinity(0))
+    cpu_model = cpu_model_name()
     n_heads = min(n_heads, wl.B * wl.H)
     stride = max(1, (wl.B * wl.H) // n_heads)
     heads = [divmod(i * stride, wl.H) for i in range(n_heads)]
@@ -125,6 +138,8 @@ def cpu_baseline(x, wl, causal: bool, n_heads: int) -> dict:
         "kind": "oracle",
         "cpu_model": cpu_model,
         "blas": blas,
+        "blas_threads": blas_threads,
+        "parallelism": "heads one after another, each with the BLAS library's own threads",
         "sample": (f"{len(heads)} of {wl.B * wl.H} heads of one step (forward + backward, "
                    f"N={wl.N}, d={wl.d}, {'causal' if causal else 'full'}), float64 numpy, "
                    f"{dt:.2f} s; "
@@ -245,6 +260,156 @@ def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
                     "fp8_frac_of_fp8_peak": round(f / t8 / 1e9 / PEAK_FP8_TFLOPS, 4),
                     "bf16_ms": round(t16, 4), "bf16_tflops": round(f / t16 / 1e9, 2),
                     "speedup": round(t16 / t8, 3)})
+    return out
+
+
+def _event_times(fn, iters: int, warmup: int) -> list:
+    """Per-launch times (ms) of ``fn`` from HIP events on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def _oracle_sample(x, wl, causal: bool, q_mult: float) -> dict:
+    """The fp64 oracle's forward on a bounded sample of one workload,
+    timed here, with the whole workload's time extrapolated from it."""
+    import numpy as np
+    import oracle
+    BH = wl.B * wl.H
+    if wl.N <= 4096:
+        n = {"c1": 1, "c2": 4, "c3": 4}.get(wl.name, 2)
+        heads = [divmod(i * max(1, BH // n), wl.H) for i in range(min(n, BH))]
+        t0 = time.perf_counter()
+        for b, h in heads:
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.attention_forward(x["q"][sl], x["k"][sl], x["v"][sl], wl.scale, causal)
+        dt = time.perf_counter() - t0
+        frac = len(heads) / BH
+        what = f"{len(heads)} of {BH} whole heads"
+    else:
+        rows = np.linspace(0, wl.N - 1, 512).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention_forward_rows(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.scale, causal,
+                                      rows)
+        dt = time.perf_counter() - t0
+        frac = len(rows) / (BH * wl.N)
+        what = f"{len(rows)} evenly spaced query rows of 1 of {BH} heads"
+    f_sample = wl.flops_fwd(causal) * frac
+    return {"sample": f"{what}, forward, float64 numpy, full score rows", "sample_s": round(dt, 4),
+            "est_full_config_s": round(dt / frac, 4),
+            "tflops": round(f_sample / dt / 1e12, 6)}
+
+
+def configs_measure(fa, make_inputs, with_oracle: bool, iters: int = 50) -> list:
+    """Every named workload's forward (and, where it has one, backward)
+    timed on its own with HIP events on the current stream: median and
+    minimum per launch, TFLOP/s and % of the bf16 peak by the metric's flop
+    convention; beside it the fp64 oracle on a sample of the same inputs."""
+    import numpy as np
+    import torch
+    from exact_attention_flash_amd.inputs import WORKLOADS
+    out = []
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda().contiguous()
+
+    for name, wl in WORKLOADS.items():
+        B, H, N, d = wl.B, wl.H, wl.N, wl.d
+        for causal in wl.causal:
+            for q_mult in wl.q_mults:
+                x = make_inputs(B, H, N, d, seed=wl.seed, q_mult=q_mult, with_dout=wl.backward)
+                q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+                fwd = _event_times(lambda: fa.flash_attn_fwd(q, k, v, causal=causal,
+                                                             softmax_scale=wl.scale, out=o,
+                                                             lse=lse), iters, 20)
+                f_fwd = wl.flops_fwd(causal)
+                tag = (f"{name}: {'causal' if causal else 'full'} B={B} H={H} N={N} d={d}"
+                       + (f", Q x {q_mult:g}" if q_mult != 1.0 else ""))
+                rec = {"workload": tag, "pass": "fwd",
+                       "median_ms": round(fwd[len(fwd) // 2], 4), "min_ms": round(fwd[0], 4),
+                       "tflops": round(f_fwd / (fwd[len(fwd) // 2] * 1e-3) / 1e12, 2)}
+                rec["pct_of_bf16_peak"] = round(100 * rec["tflops"] / PEAK_BF16_TFLOPS, 2)
+                if wl.backward:
+                    do = dev(x["do"])
+                    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                    ws = torch.empty(fa.flash_attn_bwd_workspace_bytes(B, H, N, d),
+                                     dtype=torch.uint8, device=q.device)
+                    bwd = _event_times(lambda: fa.flash_attn_bwd(
+                        do, q, k, v, o, lse, causal=causal, softmax_scale=wl.scale, dq=dq, dk=dk,
+                        dv=dv, workspace=ws), iters, 10)
+                    f_bwd = wl.flops_bwd(causal)
+                    bm = bwd[len(bwd) // 2]
+                    rec.update({"pass": "fwd, bwd", "bwd_median_ms": round(bm, 4),
+                                "bwd_min_ms": round(bwd[0], 4),
+                                "bwd_tflops": round(f_bwd / (bm * 1e-3) / 1e12, 2),
+                                "fwd_bwd_tflops": round((f_fwd + f_bwd) / (
+                                    (fwd[len(fwd) // 2] + bm) * 1e-3) / 1e12, 2)})
+                    rec["fwd_bwd_pct_of_bf16_peak"] = round(
+                        100 * rec["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+                if with_oracle:
+                    rec["oracle"] = _oracle_sample(x, wl, causal, q_mult)
+                out.append(rec)
+                del q, k, v, o, lse
+    return out
+
+
+# Decode shapes (B, H, N_kv, d): one new query per head against a long key /
+# value cache, full attention.
+DECODE_SHAPES = [(1, 16, 16384, 128), (1, 16, 65536, 128), (8, 8, 16384, 128)]
+DECODE_SPLITS = [1, 4, 8, 16, 32, 64, 128]
+
+
+def decode_measure(fa, make_inputs, iters: int = 50) -> list:
+    """The split-KV forward on decode steps (N_q = 1): one range per head
+    (the plain forward's grid, B * H workgroups) against the key tiles cut
+    into num_splits ranges, timed with HIP events on the current stream.
+    K and V are the step's compulsory traffic; their bytes per median time
+    are reported against the 8 TB/s HBM peak."""
+    import numpy as np
+    import torch
+    out = []
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda().contiguous()
+
+    for B, H, Nk, d in DECODE_SHAPES:
+        xq = make_inputs(B, H, 1, d, seed=8000 + Nk)
+        xk = make_inputs(B, H, Nk, d, seed=8001 + Nk)
+        q, k, v = dev(xq["q"]), dev(xk["k"]), dev(xk["v"])
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+        kv_bytes = 2.0 * B * H * Nk * d * 2
+        rec = {"shape": f"decode B={B} H={H} N_q=1 N_kv={Nk} d={d}", "by_splits": {}}
+        for S in DECODE_SPLITS:
+            ws = torch.empty(fa.flash_attn_fwd_splitkv_workspace_bytes(B, H, 1, d, S),
+                             dtype=torch.uint8, device=q.device)
+            t = _event_times(lambda: fa.flash_attn_fwd_splitkv(q, k, v, S, causal=False, out=o,
+                                                               lse=lse, workspace=ws), iters, 5)
+            med = t[len(t) // 2]
+            rec["by_splits"][str(S)] = {"median_ms": round(med, 4), "min_ms": round(t[0], 4),
+                                        "kv_gbs": round(kv_bytes / (med * 1e-3) / 1e9, 1)}
+        plain = rec["by_splits"]["1"]["median_ms"]
+        best = min(rec["by_splits"], key=lambda s: rec["by_splits"][s]["median_ms"])
+        rec.update({"plain_ms": plain, "best_splits": int(best),
+                    "best_ms": rec["by_splits"][best]["median_ms"],
+                    "speedup": round(plain / rec["by_splits"][best]["median_ms"], 2),
+                    "best_kv_frac_of_hbm_peak": round(
+                        rec["by_splits"][best]["kv_gbs"] / PEAK_HBM_GBS, 4)})
+        out.append(rec)
     return out
 
 
@@ -481,6 +646,10 @@ def main() -> int:
     if args.fp8:
         from exact_attention_flash_amd.inputs import make_inputs_fp8
         line["fp8_forward"] = fp8_measure(fa, make_inputs, make_inputs_fp8)
+    if not args.no_configs:
+        line["configs"] = configs_measure(fa, make_inputs, with_oracle=args.cpu_heads > 0)
+    if not args.no_decode:
+        line["decode"] = decode_measure(fa, make_inputs)
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(x, wl, causal, args.cpu_heads)
     print(json.dumps(line), flush=True)

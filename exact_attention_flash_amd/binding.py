@@ -60,7 +60,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                 i64, i64, i64, i64, ci, fl, vp]
         lib.flash_attn_bwd_q_blocks.restype = ci
         lib.flash_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                               i64, i64, i64, i64, ci, fl, i64, vp]
+                                               i64, i64, i64, i64, i64, ci, fl, i64, vp]
         lib.flash_attn_fwd_splitkv.restype = ci
         lib.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         lib.flash_attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
@@ -229,8 +229,17 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                            lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                            stream=None):
     """``flash_attn_fwd`` with each query block's keys cut into ``num_splits``
-    ranges and merged; returns ``(out, lse)``."""
-    B, H, N, d = _check_tensors(q, k, v, names="q,k,v")
+    ranges and merged; returns ``(out, lse)``.  ``q`` is ``[B, H, N_q, d]``
+    and ``k``, ``v`` are ``[B, H, N_kv, d]``; N_q != N_kv (a decode step)
+    needs ``causal=False``."""
+    _check_tensors(k, v, names="k,v")
+    if q.dim() != 4 or tuple(q.shape[:2]) != tuple(k.shape[:2]) or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q {tuple(q.shape)} must be [B, H, N_q, d] with k's B, H and d "
+                         f"(k is {tuple(k.shape)})")
+    B, H, N, d = _check_tensors(q, names="q")
+    Nk = int(k.shape[2])
+    if q.device != k.device:
+        raise ValueError("q and k must be on one device")
     scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -240,7 +249,7 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
             or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+        raise ValueError("lse must be a contiguous float32 [B, H, N_q] tensor on q's device")
     lib = load_library()
     need = int(lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, int(num_splits)))
     if workspace is None:
@@ -251,7 +260,7 @@ def flash_attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         st = lib.flash_attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                         lse.data_ptr(), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(),
-                                        B, H, N, d, int(bool(causal)), scale, int(num_splits),
+                                        B, H, N, Nk, d, int(bool(causal)), scale, int(num_splits),
                                         _stream_ptr(q.device, stream))
     _check(st)
     return out, lse

@@ -193,6 +193,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a->o = static_cast<uint16_t*>(o);
   a->lse = lse;
   a->N = int(N);
+  a->Nk = int(N);
   a->BH = int(B * H);
   a->scale_log2 = softmax_scale * 1.4426950408889634f;
   if (drop) a->drop = *drop;
@@ -300,28 +301,34 @@ size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, i
 
 int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
-                           int64_t N, int64_t d, int causal, float softmax_scale,
+                           int64_t N_q, int64_t N_kv, int64_t d, int causal, float softmax_scale,
                            int64_t num_splits, void* stream) {
   bool empty = false;
-  int st = check_shape(B, H, N, d, &empty);
+  int st = check_shape(B, H, N_q, d, &empty);
   if (st != FA_OK) return st;
+  bool no_keys = false;
+  if ((st = check_shape(B, H, N_kv, d, &no_keys)) != FA_OK) return st;
+  // the causal mask is defined for equal lengths only; and a query needs at
+  // least one key
+  if ((causal && N_q != N_kv) || (!empty && N_kv == 0)) return FA_ERR_BAD_SHAPE;
   if ((st = check_scale(softmax_scale)) != FA_OK) return st;
   if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_BAD_SPLITS;
   if (empty) return FA_OK;
   // the partial kernel's grid: 256-row query blocks x heads x ranges
-  if (((N + 255) / 256) * (B * H) * num_splits > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if (((N_q + 255) / 256) * (B * H) * num_splits > INT32_MAX) return FA_ERR_BAD_SHAPE;
   if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(workspace, 16))
     return FA_ERR_MISALIGNED;
-  const size_t need = splitkv_ws_bytes(B, H, N, d, num_splits);
+  const size_t need = splitkv_ws_bytes(B, H, N_q, d, num_splits);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-  const size_t tb = size_t(B * H * N * d) * 2, lb = size_t(B * H * N) * 4;
-  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-  const Range outs[3] = {range_of(o, tb), range_of(lse, lb), range_of(workspace, need)};
+  const size_t qb = size_t(B * H * N_q * d) * 2, kb = size_t(B * H * N_kv * d) * 2,
+               lb = size_t(B * H * N_q) * 4;
+  const Range ins[3] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+  const Range outs[3] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, need)};
   if (any_alias(outs, 3, ins, 3)) return FA_ERR_ALIASING;
 
-  const size_t rows = size_t(num_splits) * size_t(B * H) * size_t(N);
+  const size_t rows = size_t(num_splits) * size_t(B * H) * size_t(N_q);
   char* ws = static_cast<char*>(workspace);
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -329,7 +336,8 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   a.v = static_cast<const uint16_t*>(v);
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
-  a.N = int(N);
+  a.N = int(N_q);
+  a.Nk = int(N_kv);
   a.BH = int(B * H);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.splits = int(num_splits);

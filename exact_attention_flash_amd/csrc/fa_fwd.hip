@@ -36,10 +36,9 @@
 //    operand of O^T += V^T P^T;
 //  * the V^T operand of that product is read from the row-major V tile with
 //    the transposing LDS read (ds_read_b64_tr_b16);
-//  * exponentials are base 2 with log2(e) folded into the scale, and the
-//    running max is only moved (and O, l rescaled) when a tile's max exceeds
-//    it by more than 2^8: until then the probabilities are taken relative to
-//    the stale max, which changes nothing after the final division by l;
+//  * exponentials are base 2 with log2(e) folded into the scale; the running
+//    max (and with it O and l) is moved only on tiles that raise some row's
+//    max, a branch the whole wave takes or skips;
 //  * causal: key tiles past the block's last query are never loaded, tiles
 //    past a wave's last query are skipped by that wave, and only tiles that
 //    straddle the diagonal (or the ragged end of the sequence) are masked.
@@ -62,8 +61,14 @@ struct FwdCfg {
 };
 
 // Largest growth of the probabilities (in log2 units) tolerated before the
-// running max is moved.
-constexpr float kRescaleThreshold = 8.f;
+// running max is moved.  Zero: the max moves whenever a tile raises it, so
+// the largest probability of every row is exactly 1 when it is rounded to
+// bf16 for the P V product.  With a stale max (a threshold of 8 was used
+// before) the dominant probability of a nearly one-hot row is some 2^x,
+// rounded with a relative error up to 2^-9, and that error lands on O
+// undivided: up to 0.018 on rows of large logits (Q x 8, |V| ~ 4), past the
+// 1e-2 bar.
+constexpr float kRescaleThreshold = 0.f;
 
 // Per-lane source offsets of the asynchronous tile copies.  Copy t of a lane
 // fills 16-byte slot (t * NW + w) * 64 + lane of a tile: row r = slot / CPR,
@@ -143,11 +148,11 @@ struct FwdWave {
   const uint16_t* Kh;
   const uint16_t* Vh;
   const uint16_t* Qh;
-  int w, grp, lane, c32, g, N, qw0, qrow;
+  int w, grp, lane, c32, g, N, Nk, qw0, qrow;  // N queries, Nk keys per head
   int t0;       // first key tile of this workgroup's key range
   int nt, ntw;  // tiles in the range; of those, tiles this wave sees (causal)
   float sl2;
-  float m_run;   // running max of scale*log2(e)*s (possibly stale)
+  float m_run;   // running max of scale*log2(e)*s
   float l_part;  // this lane's share of the running row sum
   bf16x8 qf[D / 16];
   f32x16 oacc[D / 32];  // O^T: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
@@ -211,13 +216,13 @@ struct FwdWave {
   __device__ __forceinline__ void softmax_phase(int t) {
     if (t < 0 || t >= ntw) return;
     const int k0 = (t0 + t) * BC;
-    const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > qw0));
     if (need_mask) {
       // key k0 + 8 g + o is visible iff o <= lim (o is a compile-time offset).
       // The select is bit arithmetic on a sign mask kept opaque, so that it
       // stays in vector registers instead of 32 live compare masks in
       // scalar register pairs.
-      const int lim = opaque((CAUSAL ? min(N - 1, qrow) : N - 1) - k0 - 8 * g);
+      const int lim = opaque((CAUSAL ? min(Nk - 1, qrow) : Nk - 1) - k0 - 8 * g);
 #pragma unroll
       for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
@@ -232,8 +237,8 @@ struct FwdWave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
     mx = max_halves(mx) * sl2;
-    // Move the running max only when some query's probabilities would grow
-    // past 2^threshold (always on the first visible tile, where m = -inf).
+    // Move the running max when this tile raises it for some query of the
+    // wave (always on the first visible tile, where m = -inf).
     if (__ballot(mx > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, mx);
       // a query with every key so far masked keeps m = -inf and nothing to rescale
@@ -291,21 +296,22 @@ struct FwdWave {
   __device__ __forceinline__ void begin_item(const FwdArgs& a, int bh_, int qb, int split,
                                              int splits) {
     bh = bh_;
-    const int64_t hoff = (int64_t)bh * N * D;
-    Kh = a.k + hoff;
-    Vh = a.v + hoff;
-    Qh = a.q + hoff;
+    const int64_t koff = (int64_t)bh * Nk * D;
+    Kh = a.k + koff;
+    Vh = a.v + koff;
+    Qh = a.q + (int64_t)bh * N * D;
     const int q0 = qb * C::BR;
     qw0 = q0 + (2 * (w & 3) + grp) * C::QW;
     qrow = qw0 + c32;  // the query this lane owns
     // key tiles the block sees, then this workgroup's range of them
-    int nt_all = (N + BC - 1) / BC;
+    int nt_all = (Nk + BC - 1) / BC;
     if (CAUSAL) nt_all = min(nt_all, (q0 + C::BR + BC - 1) / BC);
     t0 = split * nt_all / splits;
     const int t1 = (split + 1) * nt_all / splits;
     nt = t1 - t0;
     const int ntw_all = CAUSAL ? min(nt_all, (qw0 + C::QW + BC - 1) / BC) : nt_all;
     ntw = max(0, min(nt, ntw_all - t0));
+    if (qw0 >= N) ntw = 0;  // no real query in this wave: copies and barriers only
     m_run = -INFINITY;
     l_part = 0.f;
   }
@@ -315,9 +321,9 @@ struct FwdWave {
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16 kc + 8 g + 0..7].
   __device__ __forceinline__ void issue_prologue(const FwdArgs& a) {
     if (nt > 0) {
-      cp.template issue<true>(Kh, sm.k[0], t0 * BC, N, w, lane);
-      if (nt > 1) cp.template issue<true>(Kh, sm.k[1], (t0 + 1) * BC, N, w, lane);
-      cp.template issue<false>(Vh, sm.v[0], t0 * BC, N, w, lane);
+      cp.template issue<true>(Kh, sm.k[0], t0 * BC, Nk, w, lane);
+      if (nt > 1) cp.template issue<true>(Kh, sm.k[1], (t0 + 1) * BC, Nk, w, lane);
+      cp.template issue<false>(Vh, sm.v[0], t0 * BC, Nk, w, lane);
     }
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
@@ -366,14 +372,14 @@ struct FwdWave {
     if (GRP == 0) {
       matrix_phase<KB, VB>(t);
     } else {
-      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, Nk, w, lane);
+      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);
       softmax_phase(t - 1);
     }
     block_barrier();
     if (GRP == 0) {
-      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, N, w, lane);
-      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, N, w, lane);
+      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, Nk, w, lane);
+      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);
       softmax_phase(t);
     } else {
       matrix_phase<KB, VB>(t);
@@ -430,6 +436,7 @@ fa_fwd_kernel(FwdArgs a) {
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
   f.N = N;
+  f.Nk = a.Nk;
   f.sl2 = a.scale_log2;
   f.trv = TrLane<D>(f.lane);
   f.kbase = f.c32 * D;

@@ -24,16 +24,18 @@ struct DropArgs {
 
 struct FwdArgs {
   const uint16_t* q;  // bf16 [B, H, N, d]
-  const uint16_t* k;
+  const uint16_t* k;  // bf16 [B, H, Nk, d]
   const uint16_t* v;
   uint16_t* o;        // bf16 [B, H, N, d]
   float* lse;         // fp32 [B, H, N], natural log
-  int N;              // sequence length
+  int N;              // queries per head
+  int Nk;             // keys per head (= N except in the split-KV forward)
   int BH;             // B * H
   float scale_log2;   // softmax_scale * log2(e), > 0
   // Split-KV forward only (splits > 1 or partials requested): each query
   // block's key tiles are cut into `splits` contiguous ranges, one
   // workgroup per range, whose unnormalised partial results go to
+  // Only this path allows Nk != N (without the causal mask).
   //   opart  fp32 [splits, B*H, N, d]  (sum of 2^(s - m) V over the range)
   //   mpart  fp32 [splits, B*H, N]     running max m, log2 units, scaled
   //   lpart  fp32 [splits, B*H, N]     sum of 2^(s - m) over the range

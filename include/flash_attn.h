@@ -66,8 +66,8 @@ enum fa_status {
   FA_ERR_MISALIGNED = 4,          /* a pointer breaks the alignment rule */
   FA_ERR_BAD_SCALE = 5,           /* softmax_scale is NaN, Inf or <= 0 */
   FA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the required size */
-  FA_ERR_ALIASING = 7,            /* an output overlaps an input or output */
-  FA_ERR_HIP = 8,                 /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 7,                 /* the HIP runtime rejected a launch */
+  FA_ERR_ALIASING = 8,            /* an output overlaps an input or output */
   FA_ERR_BAD_SPLITS = 9,          /* num_splits outside 1..128 (split-KV forward) */
   FA_ERR_BAD_DESCALE = 10,        /* an FP8 descale factor is NaN, Inf or <= 0 */
   FA_ERR_BAD_DROPOUT = 11         /* dropout_p is NaN, < 0 or rounds to 1 (see below) */
@@ -102,13 +102,23 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
  *   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,
  *   O = sum_s 2^(m_s - M) O_s / L,  LSE = (M + log2 L) ln 2
  * (m in log2 units of the scaled scores).  It fills the GPU when
- * B * H * ceil(N / 256) is small.  Results agree with flash_attn_fwd to
+ * B * H * ceil(N_q / 256) is small.  Results agree with flash_attn_fwd to
  * rounding (not bitwise: the sums are grouped differently).
- *   q, k, v, o, lse, causal, softmax_scale : as flash_attn_fwd
+ * The queries and the keys may differ in number, as in the decode step of
+ * the CMU notes (section "生成式 LLM 推理"): one new query, or a short block
+ * of them, against every cached key and value, which is the case Flash-
+ * Decoding splits the keys for.  The apxml example's interface gives the
+ * query and key/value tensors their own sequence lengths the same way.
+ *   q, o       : bf16 [B, H, N_q, d];  lse : fp32 [B, H, N_q]
+ *   k, v       : bf16 [B, H, N_kv, d]
+ *   causal     : requires N_q == N_kv (FA_ERR_BAD_SHAPE otherwise); with
+ *                N_q != N_kv every query sees every key
+ *   N_kv       : >= 1 when B * H * N_q > 0 (FA_ERR_BAD_SHAPE otherwise)
+ *   softmax_scale : as flash_attn_fwd
  *   workspace  : device memory of at least
- *                flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits)
- *                bytes, 16-byte aligned, caller-owned, no initialisation;
- *                it must not overlap any other argument
+ *                flash_attn_fwd_splitkv_workspace_bytes(B, H, N_q, d,
+ *                num_splits) bytes, 16-byte aligned, caller-owned, no
+ *                initialisation; it must not overlap any other argument
  *   num_splits : 1 .. 128 key ranges per query block (ranges with no key a
  *                query sees contribute nothing); FA_ERR_BAD_SPLITS otherwise
  * Two launches on `stream`.  Deterministic.
@@ -116,17 +126,18 @@ int flash_attn_fwd(const void* q, const void* k, const void* v,
 int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v,
                            void* o, float* lse,
                            void* workspace, size_t workspace_bytes,
-                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           int64_t B, int64_t H, int64_t N_q, int64_t N_kv, int64_t d,
                            int causal, float softmax_scale, int64_t num_splits,
                            void* stream);
 
 /*
- * Bytes of workspace flash_attn_fwd_splitkv needs: fp32 partial outputs
- * [num_splits, B*H, N, d], then the fp32 running max and row sum
- * [num_splits, B*H, N] each, every section rounded up to 256 bytes.  Returns
- * 0 for an empty problem and for invalid sizes or num_splits.
+ * Bytes of workspace flash_attn_fwd_splitkv needs for N_q queries per
+ * head: fp32 partial outputs [num_splits, B*H, N_q, d], then the fp32
+ * running max and row sum [num_splits, B*H, N_q] each, every section
+ * rounded up to 256 bytes (the key length does not enter).  Returns 0 for an
+ * empty problem and for invalid sizes or num_splits.
  */
-size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+size_t flash_attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N_q, int64_t d,
                                               int64_t num_splits);
 
 /*
@@ -230,6 +241,12 @@ int flash_attn_bwd_dropout(const void* q, const void* k, const void* v,
  * row vectors [B*H, Npad] (the rowsum(dO o O) term D and LSE in base 2; Npad
  * is N rounded up to a multiple of 64), each rounded up to 256 bytes.
  * Returns 0 for an empty problem and for invalid sizes.
+ * The two vectors are the per-row statistics the backward pass works from:
+ * the stored sum of exponentials it recomputes the probabilities with
+ * ("FlashAttention 系列技术详解", section "反向传播步骤"; the FlashAttention-2
+ * forward keeps only that one statistic, section "具体优化策略"), and the
+ * per-row softmax-gradient term of "FlashAttention 的基本原理" (section 2.4).
+ * The caller owns the memory so that the library never allocates.
  */
 size_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
@@ -289,7 +306,15 @@ int flash_attn_bwd_q_blocks(const void* q, const void* k, const void* v,
                             int64_t B, int64_t H, int64_t N, int64_t d,
                             int causal, float softmax_scale, void* stream);
 
-/* Static, human-readable text for a status code ("unknown status" if none). */
+/*
+ * Static, human-readable text for a status code ("unknown status" if none).
+ * An unsupported configuration is reported, never rerouted: the apxml
+ * example ("优化的注意力实现 (FlashAttention)") catches the RuntimeError of
+ * an optimised attention kernel that fails or does not support its inputs
+ * and falls back, on the caller's side, to the plain implementation.  The
+ * library returns the status and this text and leaves any fallback to the
+ * caller.
+ */
 const char* flash_attn_status_string(int status);
 
 #ifdef __cplusplus

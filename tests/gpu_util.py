@@ -4,8 +4,10 @@ device, and the tolerance checks of the parity bar.
 Tolerances (fixed by the project's acceptance bar):
   * O (bf16 output): |O_gpu - O_ref| <= 1e-2, plus half a bf16 ulp of O_ref
     (a correctly rounded bf16 value with |O| >= 4 can be off by more than
-    1e-2 from the exact value; the count of elements that needed the
-    allowance is reported);
+    1e-2 from the exact value, and in nearly one-hot rows the bf16 rounding
+    of the probabilities adds to that; the count of elements that needed
+    the allowance is reported).  Tests of N(0, 1) inputs without the Q x 8
+    variant use the plain 1e-2 bar (``strict``);
   * LSE: |LSE_gpu - LSE_ref| <= 1e-3;
   * dQ, dK, dV: max |g_gpu - g_ref| <= 5e-2 * max |g_ref|, per tensor.
 """
@@ -40,10 +42,16 @@ def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
 
 
-def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "O") -> dict:
+def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "O", strict: bool = False) -> dict:
+    """O against the oracle.  ``strict``: the plain 1e-2 bar, no allowance
+    (for inputs whose outputs stay small, where the allowance is never
+    needed: every N(0, 1) workload without the Q x 8 variant)."""
     err = np.abs(o_gpu - o_ref)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     plain = err <= O_ATOL
+    if strict:
+        assert np.all(plain), (f"{what}: {int((~plain).sum())} elements beyond 1e-2; "
+                               f"max err {err.max():.3e}")
     allowed = err <= O_ATOL + half_ulp_bf16(o_ref)
     bad = ~allowed
     assert not np.any(bad), (
@@ -124,3 +132,17 @@ def check_o_fp8(o_gpu, o_ref, a_abs, floor, sigma2, what="O (fp8)") -> dict:
 def fp8_to_device(codes: np.ndarray, device="cuda") -> torch.Tensor:
     """uint8 E4M3 codes -> contiguous uint8 tensor on the GPU."""
     return torch.from_numpy(np.ascontiguousarray(codes)).to(device).contiguous()
+
+
+def persistent_grid(items: int) -> int:
+    """Workgroups of a persistent kernel over ``items`` work items on this
+    device: one per compute unit, never more than the items, a multiple of 8
+    when at least 8 (the library's rule)."""
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    g = min(items, cus)
+    return g & ~7 if g >= 8 else g
+
+
+def most_items_per_workgroup(items: int) -> int:
+    g = persistent_grid(items)
+    return -(-items // g)

@@ -19,7 +19,18 @@ from exact_attention_flash_amd.binding import LIB_PATH, load_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, ALIAS, HIPERR, SPLITS, DESCALE, DROPOUT = range(12)
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, HIPERR, ALIAS, SPLITS, DESCALE, DROPOUT = \
+    range(12)
+
+
+def test_status_enum_matches_header():
+    text = open(HEADER).read()
+    enum = dict((n, int(v)) for n, v in re.findall(r"\b(FA_\w+)\s*=\s*(\d+)", text))
+    assert enum == {"FA_OK": FA_OK, "FA_ERR_NULL_POINTER": NULLP, "FA_ERR_BAD_SHAPE": SHAPE,
+                    "FA_ERR_UNSUPPORTED_HEAD_DIM": HEADDIM, "FA_ERR_MISALIGNED": MISAL,
+                    "FA_ERR_BAD_SCALE": SCALE, "FA_ERR_WORKSPACE_TOO_SMALL": WS,
+                    "FA_ERR_HIP": HIPERR, "FA_ERR_ALIASING": ALIAS, "FA_ERR_BAD_SPLITS": SPLITS,
+                    "FA_ERR_BAD_DESCALE": DESCALE, "FA_ERR_BAD_DROPOUT": DROPOUT}
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                             reason="fake-pointer validation runs only without a GPU")
@@ -107,11 +118,11 @@ def test_fwd_validation():
 
 
 def _fwd_split(lib, ws_bytes=None, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, ws=6 * A, B=1, H=1,
-               N=16, d=64, causal=0, scale=0.125, splits=2):
+               N=16, d=64, causal=0, scale=0.125, splits=2, Nk=None):
     need = lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits)
     wsb = need if ws_bytes is None else ws_bytes
-    return lib.flash_attn_fwd_splitkv(q, k, v, o, lse, ws, wsb, B, H, N, d, causal, scale, splits,
-                                      None)
+    return lib.flash_attn_fwd_splitkv(q, k, v, o, lse, ws, wsb, B, H, N, N if Nk is None else Nk,
+                                      d, causal, scale, splits, None)
 
 
 @no_gpu
@@ -130,6 +141,16 @@ def test_fwd_splitkv_validation():
     assert _fwd_split(lib, ws=A) == ALIAS                    # workspace on top of Q
     assert _fwd_split(lib, ws=4 * A) == ALIAS                # workspace on top of O
     assert _fwd_split(lib, o=3 * A) == ALIAS                 # O on top of V
+    # queries and keys of different lengths (a decode step): full attention only
+    assert _fwd_split(lib, N=1, Nk=16, causal=1) == SHAPE
+    assert _fwd_split(lib, N=16, Nk=0) == SHAPE               # a query needs a key
+    assert _fwd_split(lib, N=16, Nk=-1) == SHAPE
+    assert _fwd_split(lib, N=0, Nk=5, ws=None) == FA_OK       # no query: no-op
+    assert _fwd_split(lib, N=1, Nk=64, d=96) == HEADDIM
+    # the K / V ranges are sized by N_kv (K of 64 Ki keys reaches O at 4 A),
+    # the Q / O ranges by N_q (Q of 64 Ki queries reaches O at 3 A + 4096)
+    assert _fwd_split(lib, N=1, Nk=64 * 1024, v=3 * A + 16) == ALIAS
+    assert _fwd_split(lib, N=64 * 1024, Nk=1, ws_bytes=1 << 30, v=3 * A, o=3 * A + 4096) == ALIAS
 
 
 def _fwd_fp8(lib, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, N=16, d=64, causal=0,

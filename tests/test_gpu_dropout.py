@@ -197,3 +197,45 @@ def test_dropout_full_size_sampled(name, B, H, N, d, causal, p, seed):
     check_grad(bf16_to_f64(dq[b, h]), dQ, "dQ")
     check_grad(bf16_to_f64(dk[b, h]), dK, "dK")
     check_grad(bf16_to_f64(dv[b, h]), dV, "dV")
+
+
+# Shapes whose persistent dropout forward and key-block pass give some
+# workgroup more than one item (snake order and the round-robin fallback).
+WALKS_DROPOUT = [
+    # (B, H, N, d, causal, p, seed)
+    (2, 20, 4096, 128, False, 0.1, 5300),  # forward 640, key blocks 1280 items
+    (1, 33, 2100, 128, True, 0.2, 5301),   # forward 297, key blocks 561: round robin
+    (2, 20, 4096, 64, True, 0.15, 5302),   # d = 64, causal
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,p,seed", WALKS_DROPOUT)
+def test_dropout_walk(B, H, N, d, causal, p, seed):
+    _say(f"dropout walk B={B} H={H} N={N} d={d} causal={causal} p={p}")
+    from gpu_util import most_items_per_workgroup
+    assert most_items_per_workgroup(B * H * -(-N // 256)) > 1
+    assert most_items_per_workgroup(B * H * -(-N // 128)) > 1
+    x = make_inputs(B, H, N, d, seed=seed, with_dout=True)
+    scale = default_scale(d)
+    rs, off = 99 + seed, 3
+    (q, k, v), o, lse = _fwd(x, causal, scale, p, rs, off)
+    dq, dk, dv = flash_attn_bwd_dropout(to_device(x["do"]), q, k, v, o, lse, p, rs, off,
+                                        causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.integers(0, N, 12)]))
+    BH = B * H
+    for bh in sorted({0, BH - 1}):
+        b, h = divmod(bh, H)
+        O_ref, L_ref = oracle.attention_forward_dropout_rows(
+            x["q"][b, h], x["k"][b, h], x["v"][b, h], scale, causal, p, rs, off, bh, rows)
+        og = bf16_to_f64(o[b, h][torch.as_tensor(rows, device=o.device)])
+        check_o(og, O_ref, f"O head {bh}")
+        check_lse(lse[b, h].cpu().numpy()[rows].astype(np.float64), L_ref)
+    # one whole head's gradients (the last, so a late item of the walk)
+    b, h = divmod(BH - 1, H)
+    dQ, dK, dV = oracle.attention_backward_dropout_head(
+        x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], scale, causal, p, rs, off, BH - 1)
+    check_grad(bf16_to_f64(dq[b, h]), dQ, "dQ")
+    check_grad(bf16_to_f64(dk[b, h]), dK, "dK")
+    check_grad(bf16_to_f64(dv[b, h]), dV, "dV")

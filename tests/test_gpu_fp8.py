@@ -20,6 +20,7 @@ from exact_attention_flash_amd import flash_attn_fwd_fp8
 from exact_attention_flash_amd.inputs import default_scale, make_inputs_fp8
 
 from gpu_util import (bf16_to_f64, check_lse, check_o, check_o_fp8, fp8_error_terms,
+                      most_items_per_workgroup,
                       fp8_to_device)
 
 pytestmark = pytest.mark.gpu
@@ -174,6 +175,44 @@ def test_fwd_fp8_full_size_sampled(name, B, H, N, d, causal, seed):
         a_abs, floor, sig2 = fp8_error_terms(q, k, v, scale, causal, rows)
         og = bf16_to_f64(o[b, h][torch.as_tensor(rows, device=o.device)])
         check_o_fp8(og, O_ref, a_abs, floor, sig2, f"O (fp8) head {b},{h}")
+        check_lse(lse[b, h].cpu().numpy()[rows].astype(np.float64), L_ref)
+
+
+# Shapes whose persistent FP8 forward gives some workgroup more than one
+# (head, 256-row query block) item: snake order and the round-robin
+# fallback (item count not a multiple of 8), both masks, both head dims.
+WALKS_FP8 = [
+    # (B, H, N, d, causal, seed)
+    (2, 20, 4096, 128, False, 6100),   # 640 items
+    (1, 33, 2100, 128, True, 6101),    # 297 items: round robin
+    (2, 20, 4096, 64, True, 6102),     # 640 items, d = 64
+    (1, 33, 2100, 64, False, 6103),    # 297 items, d = 64, full attention
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,seed", WALKS_FP8)
+def test_fwd_fp8_walk(B, H, N, d, causal, seed):
+    _say(f"fp8 fwd walk B={B} H={H} N={N} d={d} causal={causal}")
+    items = B * H * -(-N // 256)
+    assert most_items_per_workgroup(items) > 1, items
+    x = make_inputs_fp8(B, H, N, d, seed=seed)
+    scale = default_scale(d)
+    o, lse = _run(x, causal, scale)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.integers(0, N, 12)]))
+    BH = B * H
+    for bh in sorted({0, BH - 1, int(rng.integers(BH))}):
+        b, h = divmod(bh, H)
+        xs = {n: x[n][b, h] for n in ("q", "k", "v")}
+        O_ref, L_ref = oracle.attention_forward_fp8_rows(
+            xs["q"], xs["k"], xs["v"], x["descale_q"], x["descale_k"], x["descale_v"],
+            scale, causal, rows)
+        q = oracle.dequantize(xs["q"], x["descale_q"])
+        k = oracle.dequantize(xs["k"], x["descale_k"])
+        v = oracle.dequantize(xs["v"], x["descale_v"])
+        a_abs, floor, sig2 = fp8_error_terms(q, k, v, scale, causal, rows)
+        og = bf16_to_f64(o[b, h][torch.as_tensor(rows, device=o.device)])
+        check_o_fp8(og, O_ref, a_abs, floor, sig2, f"O (fp8) head {bh}")
         check_lse(lse[b, h].cpu().numpy()[rows].astype(np.float64), L_ref)
 
 

@@ -18,7 +18,8 @@ import oracle
 from exact_attention_flash_amd import flash_attn_bwd, flash_attn_fwd, flash_attn_fwd_splitkv
 from exact_attention_flash_amd.inputs import WORKLOADS, default_scale, make_inputs
 
-from gpu_util import (bf16_to_f64, check_grad, check_lse, check_o, to_device)
+from gpu_util import (bf16_to_f64, check_grad, check_lse, check_o, most_items_per_workgroup,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +69,7 @@ def test_fwd_small_full_parity(B, H, N, d, causal):
     scale = default_scale(d)
     _, o, lse = _run_fwd(x, causal, scale)
     O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
-    check_o(bf16_to_f64(o), O_ref)
+    check_o(bf16_to_f64(o), O_ref, strict=True)
     check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
 
 
@@ -93,6 +94,36 @@ def test_fwd_splitkv_small_full_parity(B, H, N, d, causal, splits):
     _, o, lse = _run_fwd_split(x, causal, scale, splits)
     O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
     check_o(bf16_to_f64(o), O_ref)
+    check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
+
+
+DECODE = [
+    # (B, H, N_q, N_kv, d, num_splits): a decode step (one query, or a short
+    # block of them, against a long key/value cache), full attention
+    (1, 16, 1, 16384, 128, 16),
+    (1, 16, 1, 16384, 128, 1),
+    (2, 4, 1, 1000, 64, 8),
+    (1, 8, 64, 8192, 128, 32),
+    (1, 2, 7, 5003, 128, 5),
+    (1, 4, 1, 65536, 128, 64),
+    (2, 3, 300, 70, 64, 3),     # more queries than keys
+    (1, 1, 1, 1, 128, 4),       # a single key: three empty ranges
+    (1, 1, 33, 130, 64, 128),   # more ranges than key tiles
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,splits", DECODE)
+def test_fwd_splitkv_decode_parity(B, H, Nq, Nk, d, splits):
+    _say(f"split-KV decode B={B} H={H} N_q={Nq} N_kv={Nk} d={d} splits={splits}")
+    xq = make_inputs(B, H, Nq, d, seed=31 * Nq + d)
+    xk = make_inputs(B, H, Nk, d, seed=17 * Nk + d + 1)
+    scale = default_scale(d)
+    q, k, v = to_device(xq["q"]), to_device(xk["k"]), to_device(xk["v"])
+    o, lse = flash_attn_fwd_splitkv(q, k, v, splits, causal=False, softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert o.shape == (B, H, Nq, d) and lse.shape == (B, H, Nq)
+    O_ref, L_ref = oracle.attention_forward(xq["q"], xk["k"], xk["v"], scale, False)
+    check_o(bf16_to_f64(o), O_ref, strict=True)
     check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
 
 
@@ -190,10 +221,10 @@ def _fwd_workload(name, causal, q_mult, full_heads_max, splits=None):
         heads = [heads[i] for i in sorted(set(pick.tolist()) | {0, len(heads) - 1})]
     stats = []
     for b, h in heads:
-        rows = np.arange(wl.N) if wl.N <= 2048 else _sample_rows(wl.N, rng)
+        rows = np.arange(wl.N) if wl.N <= 2048 else _sample_rows(wl.N, rng, n=48)
         Or, Lr = oracle.attention_forward_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h],
                                                wl.scale, causal, rows)
-        stats.append(check_o(o64[b, h, rows], Or, f"O[{b},{h}]"))
+        stats.append(check_o(o64[b, h, rows], Or, f"O[{b},{h}]", strict=q_mult == 1.0))
         check_lse(l64[b, h, rows], Lr, f"LSE[{b},{h}]")
     # every head, every row: finite, and LSE >= max visible score is implied
     # by LSE >= ln(1) + ... ; check the cheap bound LSE > -inf and O within
@@ -207,41 +238,45 @@ def _fwd_workload(name, causal, q_mult, full_heads_max, splits=None):
          f"ulp allowance used {sum(s['needed_ulp_allowance'] for s in stats)}")
 
 
+ALL_HEADS = 1 << 30
+
+
 def test_workload_c1():
-    _fwd_workload("c1", False, 1.0, 1)
+    _fwd_workload("c1", False, 1.0, ALL_HEADS)
 
 
 def test_workload_c2():
-    _fwd_workload("c2", True, 1.0, 16)
+    _fwd_workload("c2", True, 1.0, ALL_HEADS)
 
 
 def test_workload_c1_splitkv():
-    _fwd_workload("c1", False, 1.0, 1, splits=2)
+    _fwd_workload("c1", False, 1.0, ALL_HEADS, splits=2)
 
 
 def test_workload_c2_splitkv():
-    _fwd_workload("c2", True, 1.0, 16, splits=4)
+    _fwd_workload("c2", True, 1.0, ALL_HEADS, splits=4)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("q_mult", [1.0, 8.0])
 def test_workload_c3(causal, q_mult):
-    _fwd_workload("c3", causal, q_mult, 12)
+    _fwd_workload("c3", causal, q_mult, ALL_HEADS)
 
 
 def test_workload_c4():
-    _fwd_workload("c4", True, 1.0, 3)
+    _fwd_workload("c4", True, 1.0, ALL_HEADS)
 
 
 def test_workload_c5_forward():
-    _fwd_workload("c5", True, 1.0, 3)
+    _fwd_workload("c5", True, 1.0, ALL_HEADS)
 
 
 def test_workload_c5_backward():
-    """Full-size C5 forward + backward as the bench runs it; two whole heads
-    against the oracle, and for every head the identities
-    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (rows of P sum to one, rows
-    of dS sum to zero)."""
+    """Full-size C5 forward + backward as the bench runs it, compared element
+    by element on every one of the 64 heads: dQ on sampled query rows and
+    dK, dV on sampled keys (block edges, the ends and random positions,
+    different per head), against the oracle's row-chunked backward, which
+    takes every query row of the head into the key gradients."""
     wl = WORKLOADS["c5"]
     _say("workload c5 backward (4,16,4096,128) causal")
     x = make_inputs(wl.B, wl.H, wl.N, wl.d, seed=wl.seed, with_dout=True)
@@ -250,20 +285,22 @@ def test_workload_c5_backward():
     dq, dk, dv = flash_attn_bwd(do, q, k, v, o, lse, causal=True, softmax_scale=wl.scale)
     torch.cuda.synchronize()
     dq64, dk64, dv64 = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
-    for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        dQ, dK, dV = oracle.attention_backward(x["q"][sl], x["k"][sl], x["v"][sl],
-                                               x["do"][sl], wl.scale, True)
-        check_grad(dq64[sl], dQ, f"dQ[{b},{h}]")
-        check_grad(dk64[sl], dK, f"dK[{b},{h}]")
-        check_grad(dv64[sl], dV, f"dV[{b},{h}]")
-    do64 = oracle.widen_bf16(x["do"])
-    sdv = dv64.sum(axis=2)
-    sdo = do64.sum(axis=2)
-    tol = 5e-2 * np.abs(dv64).max() * np.sqrt(wl.N)
-    assert np.abs(sdv - sdo).max() <= tol
-    sdk = dk64.sum(axis=2)
-    assert np.abs(sdk).max() <= 5e-2 * np.abs(dk64).max() * np.sqrt(wl.N)
+    assert np.all(np.isfinite(dq64)) and np.all(np.isfinite(dk64)) and np.all(np.isfinite(dv64))
+    rng = np.random.default_rng(wl.seed + 1)
+    N = wl.N
+    fixed = [0, 1, 63, 64, 127, 128, 255, 256, N // 2, N - 129, N - 128, N - 2, N - 1]
+    worst = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    for b in range(wl.B):
+        for h in range(wl.H):
+            idx = np.unique(np.concatenate([fixed, rng.choice(N, 12, replace=False)]))
+            xs = {n: x[n][b, h] for n in ("q", "k", "v", "do")}
+            dQ, dK, dV = oracle.attention_backward_sampled(xs["q"], xs["k"], xs["v"], xs["do"],
+                                                           wl.scale, True, idx, idx)
+            worst["dQ"] = max(worst["dQ"], check_grad(dq64[b, h, idx], dQ, f"dQ[{b},{h}]"))
+            worst["dK"] = max(worst["dK"], check_grad(dk64[b, h, idx], dK, f"dK[{b},{h}]"))
+            worst["dV"] = max(worst["dV"], check_grad(dv64[b, h, idx], dV, f"dV[{b},{h}]"))
+    _say("  worst relative errors over 64 heads: " +
+         ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
 
 
 def test_bwd_deterministic_and_staged_equals_one_call():
@@ -398,12 +435,14 @@ def test_fwd_extreme_logits(d, causal, pattern):
 
 
 WALKS = [
-    # (B, H, N, d, causal) and the key-block walk each gives on a 256-CU
-    # device (one workgroup per CU, 128-key items):
-    (1, 8, 5000, 128, True),   # 320 items: snake order, partial second round
-    (1, 8, 5000, 64, False),   # the same walk, full attention, d = 64
-    (3, 5, 2100, 128, True),   # 255 items on 248 workgroups: round robin, 7 take two
-    (2, 20, 4096, 64, True),   # 1280 items: snake order over five rounds
+    # (B, H, N, d, causal) and the walks each gives on a 256-CU device (one
+    # workgroup per CU; 256-row forward items, 128-key key-block items):
+    (1, 8, 5000, 128, True),    # key blocks: 320 items, snake order, partial second round
+    (1, 8, 5000, 64, False),    # the same walk, full attention, d = 64
+    (3, 5, 2100, 128, True),    # key blocks: 255 items on 248 workgroups, round robin
+    (2, 20, 4096, 64, True),    # key blocks: 1280 items, snake order over five rounds
+    (2, 20, 4096, 128, False),  # forward 640 items, key blocks 1280: full attention, d = 128
+    (1, 33, 2100, 128, True),   # forward 297 and key blocks 561 items: round robin in both
 ]
 
 
@@ -416,6 +455,13 @@ def test_bwd_key_block_walk(B, H, N, d, causal):
     persistent forward (several query blocks per workgroup on the largest
     shape) on the same rows."""
     _say(f"key-block walk ({B},{H},{N},{d}) causal={causal}")
+    fwd_items = B * H * -(-N // 256)
+    kv_items = B * H * -(-N // 128)
+    # the case must give some workgroup of the key-block pass (and, where
+    # the comment above says so, of the forward) more than one item here
+    assert most_items_per_workgroup(kv_items) > 1, kv_items
+    _say(f"  forward items {fwd_items} (<= {most_items_per_workgroup(fwd_items)} per workgroup), "
+         f"key-block items {kv_items} (<= {most_items_per_workgroup(kv_items)})")
     x = make_inputs(B, H, N, d, seed=7 * N + d, with_dout=True)
     scale = default_scale(d)
     (q, k, v), o, lse = _run_fwd(x, causal, scale)
