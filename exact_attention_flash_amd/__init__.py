@@ -17,6 +17,8 @@ __all__ = [
     "flash_attn_fwd_splitkv_workspace_bytes",
     "flash_attn_bwd",
     "flash_attn_bwd_workspace_bytes",
+    "flash_attn_bwd_noalloc",
+    "BWD_NOALLOC_SCRATCH_BYTES",
     "flash_attn_bwd_preprocess",
     "flash_attn_bwd_kv_blocks",
     "flash_attn_bwd_q_blocks",

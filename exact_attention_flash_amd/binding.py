@@ -77,6 +77,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.flash_attn_bwd_dropout.restype = ci
         lib.flash_attn_quantize_fp8.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i64, i64, vp, vp]
         lib.flash_attn_quantize_fp8.restype = ci
+        lib.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i64, i64, i64, i64, ci, fl, vp]
+        lib.flash_attn_bwd_noalloc.restype = ci
         lib.flash_attn_status_string.argtypes = [ci]
         lib.flash_attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -293,6 +296,35 @@ def flash_attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torc
                                 lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                 dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
                                 int(bool(causal)), scale, _stream_ptr(q.device, stream))
+    _check(st)
+    return dq, dk, dv
+
+
+# Largest workspace the allocation-free backward's static scratch holds
+# (FA_BWD_NOALLOC_SCRATCH_BYTES).
+BWD_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def flash_attn_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                           v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                           dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                           causal: bool = False, softmax_scale: float | None = None, stream=None):
+    """flash_attn_bwd into the caller's dq, dk, dv with no workspace: the
+    library keeps the row vectors in its own static device buffer, so
+    nothing is allocated (usable under stream capture).  Calls that overlap
+    on one device race on that buffer."""
+    B, H, N, d = _check_tensors(q, k, v, out, dout, dq, dk, dv,
+                                names="q,k,v,out,dout,dq,dk,dv")
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                                        int(bool(causal)), scale, _stream_ptr(q.device, stream))
     _check(st)
     return dq, dk, dv
 

@@ -254,6 +254,35 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   return FA_OK;
 }
 
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                           float softmax_scale, void* stream) {
+  static_assert(FA_BWD_NOALLOC_SCRATCH_BYTES == fa::kNoallocScratchBytes, "scratch size");
+  bool empty = false;
+  int st = check_shape(B, H, N, d, &empty);
+  if (st != FA_OK) return st;
+  if (!empty && ws_bytes(B, H, N, d) > fa::kNoallocScratchBytes) return FA_ERR_SCRATCH_TOO_SMALL;
+  // validate every caller pointer (the workspace is the library's own, so
+  // it is left out of the checks), then point the row vectors at it
+  const BwdPtrs p{q, k, v, o, lse, dout, dq, dk, dv, nullptr};
+  fa::BwdArgs a;
+  const size_t need = empty ? 0 : ws_bytes(B, H, N, d);
+  st = prepare_bwd(p, kAllBwd & ~unsigned(kWs), need, B, H, N, d, softmax_scale, &a);
+  if (st != FA_OK || a.BH == 0) return st;
+  void* scratch = nullptr;
+  if (fa::noalloc_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  const size_t prow = size_t(B * H) * size_t(padded_rows(N));
+  char* ws = static_cast<char*>(scratch);
+  a.delta = reinterpret_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(ws + round_up(prow * 4, kWsAlign));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fa::launch_bwd_pre(a, int(d), s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_kv(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_q(a, int(d), causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout, void* workspace,
                               size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
                               void* stream) {
@@ -455,6 +484,9 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 128";
     case FA_ERR_BAD_DESCALE: return "FP8 descale factors must be finite and > 0";
     case FA_ERR_BAD_DROPOUT: return "dropout_p must be >= 0 and round (in steps of 1/256) below 1";
+    case FA_ERR_SCRATCH_TOO_SMALL:
+      return "problem too large for the static scratch of flash_attn_bwd_noalloc "
+             "(B * H * ceil(N / 64) * 64 must be <= 2^20)";
     default: return "unknown status";
   }
 }

@@ -100,6 +100,16 @@ struct BwdArgs {
   DropArgs drop;
 };
 
+// Size of the library-owned device scratch of the allocation-free backward
+// entry point (one copy per device; it holds the backward pass's two fp32
+// row vectors, so at most 1 M padded rows: B * H * Npad <= 2^20).
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's copy of that scratch (looked up on the
+// first call on each device, with the device current, then cached).
+hipError_t noalloc_scratch(void** out);
+
 // Compute units of the current device (cached per device; 0 if unknown).
 inline int cu_count() {
   static std::atomic<int> cached[64];

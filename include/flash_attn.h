@@ -70,7 +70,8 @@ enum fa_status {
   FA_ERR_ALIASING = 8,            /* an output overlaps an input or output */
   FA_ERR_BAD_SPLITS = 9,          /* num_splits outside 1..128 (split-KV forward) */
   FA_ERR_BAD_DESCALE = 10,        /* an FP8 descale factor is NaN, Inf or <= 0 */
-  FA_ERR_BAD_DROPOUT = 11         /* dropout_p is NaN, < 0 or rounds to 1 (see below) */
+  FA_ERR_BAD_DROPOUT = 11,        /* dropout_p is NaN, < 0 or rounds to 1 (see below) */
+  FA_ERR_SCRATCH_TOO_SMALL = 12   /* problem needs more than the library's static scratch */
 };
 
 /*
@@ -272,6 +273,30 @@ int flash_attn_bwd(const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes,
                    int64_t B, int64_t H, int64_t N, int64_t d,
                    int causal, float softmax_scale, void* stream);
+
+/*
+ * Backward pass that allocates nothing, for callers that cannot allocate or
+ * pass device memory: code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * flash_attn_bwd (bit-identical outputs), minus the workspace: the row
+ * vectors live in a device buffer the library itself holds, one static copy
+ * of FA_BWD_NOALLOC_SCRATCH_BYTES per device for the life of the process.
+ *   FA_ERR_SCRATCH_TOO_SMALL if flash_attn_bwd_workspace_bytes(B, H, N, d)
+ *   exceeds FA_BWD_NOALLOC_SCRATCH_BYTES (B * H * Npad > 2^20 rows), before
+ *   any HIP call.
+ * The first call on a device looks up that device's buffer address (a HIP
+ * call with the device current, nothing allocated); a failed lookup is
+ * FA_ERR_HIP.  No hipMalloc, hipFree or memset is ever issued.  Every call on
+ * one device uses the same buffer and overwrites it (nothing in it needs to
+ * start at zero): calls that overlap in time on one device, for example on
+ * two streams, race and must not be issued.
+ */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           int causal, float softmax_scale, void* stream);
 
 /*
  * The three stages of flash_attn_bwd as separate calls, one kernel launch

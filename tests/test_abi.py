@@ -19,8 +19,8 @@ from exact_attention_flash_amd.binding import LIB_PATH, load_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, HIPERR, ALIAS, SPLITS, DESCALE, DROPOUT = \
-    range(12)
+FA_OK, NULLP, SHAPE, HEADDIM, MISAL, SCALE, WS, HIPERR, ALIAS, SPLITS, DESCALE, DROPOUT, \
+    SCRATCH = range(13)
 
 
 def test_status_enum_matches_header():
@@ -30,7 +30,8 @@ def test_status_enum_matches_header():
                     "FA_ERR_UNSUPPORTED_HEAD_DIM": HEADDIM, "FA_ERR_MISALIGNED": MISAL,
                     "FA_ERR_BAD_SCALE": SCALE, "FA_ERR_WORKSPACE_TOO_SMALL": WS,
                     "FA_ERR_HIP": HIPERR, "FA_ERR_ALIASING": ALIAS, "FA_ERR_BAD_SPLITS": SPLITS,
-                    "FA_ERR_BAD_DESCALE": DESCALE, "FA_ERR_BAD_DROPOUT": DROPOUT}
+                    "FA_ERR_BAD_DESCALE": DESCALE, "FA_ERR_BAD_DROPOUT": DROPOUT,
+                    "FA_ERR_SCRATCH_TOO_SMALL": SCRATCH}
 
 no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                             reason="fake-pointer validation runs only without a GPU")
@@ -50,7 +51,7 @@ def test_library_exports_header_symbols():
                             "flash_attn_bwd_q_blocks", "flash_attn_fwd_splitkv",
                             "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_fwd_fp8",
                             "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
-                            "flash_attn_quantize_fp8"])
+                            "flash_attn_quantize_fp8", "flash_attn_bwd_noalloc"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True)
@@ -61,7 +62,7 @@ def test_library_exports_header_symbols():
 
 def test_status_strings():
     lib = load_library()
-    for s in range(12):
+    for s in range(13):
         assert lib.flash_attn_status_string(s) not in (None, b"unknown status")
     assert lib.flash_attn_status_string(99) == b"unknown status"
 
@@ -292,6 +293,33 @@ def test_bwd_stage_validation():
                                        1, 2, 16, 128, 1, 0.1, None) == ALIAS
     assert lib.flash_attn_bwd_q_blocks(A, 2 * A, 3 * A, 6 * A, 7 * A, 10 * A, need,
                                        0, 2, 16, 128, 1, 0.1, None) == FA_OK
+
+
+def _bwd_noalloc(lib, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+                B=1, H=2, N=16, d=128, causal=1, scale=0.1)
+    args.update(kw)
+    return lib.flash_attn_bwd_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                      args["do"], args["dq"], args["dk"], args["dv"], args["B"],
+                                      args["H"], args["N"], args["d"], args["causal"],
+                                      args["scale"], None)
+
+
+@no_gpu
+def test_bwd_noalloc_validation():
+    """Same checks as flash_attn_bwd on every caller pointer, plus the size
+    limit of the static scratch, all before any HIP call."""
+    lib = load_library()
+    assert _bwd_noalloc(lib, H=0) == FA_OK
+    assert _bwd_noalloc(lib, do=None) == NULLP
+    assert _bwd_noalloc(lib, d=32) == HEADDIM
+    assert _bwd_noalloc(lib, dk=8 * A + 2) == MISAL
+    assert _bwd_noalloc(lib, scale=float("nan")) == SCALE
+    assert _bwd_noalloc(lib, dq=A) == ALIAS
+    # 2^20 padded rows fit; one more 64-row block does not
+    assert _bwd_noalloc(lib, B=1, H=16, N=65536, dq=7 * A) != SCRATCH
+    assert _bwd_noalloc(lib, B=1, H=16, N=65537) == SCRATCH
+    assert _bwd_noalloc(lib) == HIPERR       # valid: reaches the device, which is absent
 
 
 @no_gpu
