@@ -436,7 +436,7 @@ fa_fwd_kernel(FwdArgs a) {
   f.c32 = f.lane & 31;
   f.g = f.lane >> 5;
   f.N = N;
-  f.Nk = a.Nk;
+  f.Nk = SPLIT ? a.Nk : N;  // the same value as N outside the split-KV forward
   f.sl2 = a.scale_log2;
   f.trv = TrLane<D>(f.lane);
   f.kbase = f.c32 * D;
