@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     const int64_t rr = r0 + k * RPB;
     if (rr < rows && ch == 0) {
-      a.delta[rr] = acc;
+      a.delta[rr] = -acc;  // stored negated: the passes start dP from it
       a.lse2[rr] = real[k] ? lv[k] * kLog2e : INFINITY;
     }
   }
@@ -243,11 +243,16 @@ struct KvBlock {
     cp.issue(a.q + ho, a.dout + ho, sm.q[ST], sm.dout[ST], q0, N, w, lane);
     // LSE*log2(e) then D of the block: 2 x BRQ floats = BRQ / 2 lanes of 16
     // bytes (the rows are padded to whole blocks)
+    // (buffer copies, not global_load_lds: the compiler takes a pending
+    // global_load_lds for a possible LDS access of unknown order and then
+    // waits for every LDS read with lgkmcnt(0))
     if (w == 0 && lane < BRQ / 2) {
       constexpr int half = BRQ / 4;  // lanes per vector
       const int64_t vo = (int64_t)bh_ * a.Npad + q0;
-      const float* src = lane < half ? a.lse2 + vo + 4 * lane : a.delta + vo + 4 * (lane - half);
-      load_lds16(src, sm.vec[ST]);
+      if (lane < half)
+        buffer_load_lds16(make_rsrc(a.lse2 + vo, BRQ * 4), 16 * lane, sm.vec[ST]);
+      else
+        buffer_load_lds16(make_rsrc(a.delta + vo, BRQ * 4), 16 * (lane - half), sm.vec[ST]);
     }
   }
 
@@ -284,11 +289,16 @@ struct KvBlock {
     for (int qg = 0; qg < BRQ / 32; ++qg) {
       // lane (key, kg) gets queries q0 + 32 qg + 8 kg + j, j < 8
       if (CAUSAL && (kw0 > q0 + 32 * qg + 31)) continue;  // every key after every query
+      const int ql = 32 * qg + 8 * kg;
+      // -D of the lane's 8 queries; without dropout dP starts from it, so
+      // the products leave dP - D in the accumulator
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql + 4);
       f32x4 s[2], dp[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         s[t] = zero4();
-        dp[t] = zero4();
+        dp[t] = DROP ? zero4() : (t == 0 ? d0 : d1);
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) {
           const int o = (32 * qg + 4 * t) * D + sb + (((4 * k) ^ su) << 3);
@@ -299,18 +309,15 @@ struct KvBlock {
       // keep the Q / dO reads two slices ahead of the MFMAs that consume them
       sched_pipeline<2 * (D / 32), 2, 2, 2>();
       const bool need_mask = (kb0 + BCK > N) || (CAUSAL && kw0 + C::KW - 1 > q0 + 32 * qg);
-      const int ql = 32 * qg + 8 * kg;
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(lv + ql);
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(lv + ql + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(lv + BRQ + ql + 4);
       float p[8], ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float sv = j < 4 ? s[0][j] : s[1][j - 4];
         const float dpv = j < 4 ? dp[0][j] : dp[1][j - 4];
         const float lse = j < 4 ? l0[j] : l1[j - 4];
-        const float dlt = j < 4 ? d0[j] : d1[j - 4];
+        const float ndlt = j < 4 ? d0[j] : d1[j - 4];  // -D
         float pv = exp2_fast(fmaf(sv, sl2, -lse));
         if (need_mask) {
           const int q = q0 + ql + j;
@@ -322,10 +329,10 @@ struct KvBlock {
           const int mb = 8 * qg + j;
           const bool keep = drop_keep((uint32_t)rb[mb >> 2], mb & 3, a.drop.t);
           p[j] = keep ? pv : 0.f;
-          ds[j] = pv * fmaf(dpv, keep ? a.drop.scale : 0.f, -dlt);
+          ds[j] = pv * fmaf(dpv, keep ? a.drop.scale : 0.f, ndlt);
         } else {
           p[j] = pv;
-          ds[j] = pv * (dpv - dlt);
+          ds[j] = pv * dpv;  // dpv already holds dP - D
         }
       }
       const bf16x8 pb = pack8(p);
@@ -475,7 +482,7 @@ struct QBlock {
   const uint16_t* Kh;
   const uint16_t* Vh;
   int w, lane, c32, g, N, qw0, qrow, nt;
-  float sl2, lse2, dlt;
+  float sl2, lse2, ndlt;  // ndlt = -D of the lane's query
   bf16x8 qf[D / 16], dof[D / 16];  // B operands: Q, dO rows of this lane's query
   f32x16 dq[D / 32];                // dQ^T: lane holds dQ[qrow][32 db + 8(i/4) + 4g + i%4]
   RowLane<D> rowk;                  // row reads of K / V (row swap23(c32) of each block)
@@ -574,9 +581,9 @@ struct QBlock {
         }
         if constexpr (DROP) {
           const bool keep = drop_keep(rw[h][jj >> 2], jj & 3, drop.t);
-          t8[jj] = pv * fmaf(dp[sb][i], keep ? drop.scale : 0.f, -dlt);
+          t8[jj] = pv * fmaf(dp[sb][i], keep ? drop.scale : 0.f, ndlt);
         } else {
-          t8[jj] = pv * (dp[sb][i] - dlt);
+          t8[jj] = pv * (dp[sb][i] + ndlt);
         }
       }
       dsb[2 * sb + h] = pack8(t8);
@@ -686,7 +693,7 @@ fa_bwd_q_kernel(BwdArgs a) {
   }
   const int64_t vrow = (int64_t)bh * a.Npad + f.qrow;
   f.lse2 = real ? a.lse2[vrow] : INFINITY;  // padded rows get P = 0
-  f.dlt = real ? a.delta[vrow] : 0.f;
+  f.ndlt = real ? a.delta[vrow] : 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) f.dq[db] = zero16();
   wait_vmem();

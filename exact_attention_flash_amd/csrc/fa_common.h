@@ -165,14 +165,6 @@ namespace fa {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void global_void;
-
-// Asynchronous 16-byte copy global -> LDS.  Lane i of the wave writes its 16
-// bytes at lds_wave_base + 16 * i; lds_wave_base must be the same for every
-// lane of the wave.  Completion is tracked by the wave's vmcnt.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds_wave_base, 16, 0, 0);
-}
 
 // Buffer resource over `bytes` bytes from `base` (raw addressing, stride 0;
 // the last word is the gfx9 data-format setting for plain 32-bit access).
@@ -183,10 +175,14 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) 
                                            0x00020000);
 }
 
-// Same copy as load_lds16, through a buffer resource: lane i's 16 bytes come
-// from byte offset voff (per lane, 32-bit) of the resource.  The resource and
-// the LDS base live in scalar registers, so an address costs one VGPR and no
-// per-copy vector arithmetic.
+// Asynchronous 16-byte copy global -> LDS through a buffer resource: lane
+// i's 16 bytes come from byte offset voff (per lane, 32-bit) of the resource
+// and land at lds_wave_base + 16 * i (lds_wave_base the same for every lane
+// of the wave); completion is tracked by the wave's vmcnt.  (The
+// global_load_lds form of this copy is not used: while one is pending the
+// compiler treats LDS reads as completing out of order and waits for each
+// with lgkmcnt(0).)  The resource and the LDS base live in scalar registers,
+// so an address costs one VGPR and no per-copy vector arithmetic.
 __device__ __forceinline__ void buffer_load_lds16(buf_rsrc r, uint32_t voff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, 0, 0, 0);
 }

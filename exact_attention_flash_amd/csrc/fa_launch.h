@@ -90,7 +90,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;       // workspace: fp32 [B*H, Npad], rowsum(dO o O), 0 on padding
+  float* delta;       // workspace: fp32 [B*H, Npad], -rowsum(dO o O), 0 on padding
   float* lse2;        // workspace: fp32 [B*H, Npad], LSE * log2(e), +inf on padding
   int N;
   int Npad;           // N rounded up to kBwdQueryBlock

@@ -239,8 +239,9 @@ int flash_attn_bwd_dropout(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape: two fp32
- * row vectors [B*H, Npad] (the rowsum(dO o O) term D and LSE in base 2; Npad
- * is N rounded up to a multiple of 64), each rounded up to 256 bytes.
+ * row vectors [B*H, Npad] (the rowsum(dO o O) term D, stored negated, and
+ * LSE in base 2; Npad is N rounded up to a multiple of 64), each rounded up
+ * to 256 bytes.
  * Returns 0 for an empty problem and for invalid sizes.
  * The two vectors are the per-row statistics the backward pass works from:
  * the stored sum of exponentials it recomputes the probabilities with
@@ -306,8 +307,8 @@ int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
  * pointers it uses (the same rules as flash_attn_bwd); the workspace
  * carries the state from one stage to the next.
  *
- * flash_attn_bwd_preprocess: D_i = sum_c dO_ic O_ic and LSE * log2(e) into
- *   the workspace.  Reads o, lse, dout.
+ * flash_attn_bwd_preprocess: -D_i = -sum_c dO_ic O_ic and LSE * log2(e)
+ *   into the workspace.  Reads o, lse, dout.
  * flash_attn_bwd_kv_blocks: the pass over key blocks.  Reads q, k, v, dout
  *   and the workspace; writes dk, dv.
  * flash_attn_bwd_q_blocks: the pass over query blocks.  Reads q, k, v, dout
