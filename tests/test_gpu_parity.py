@@ -220,12 +220,13 @@ def _fwd_workload(name, causal, q_mult, full_heads_max, splits=None):
         pick = rng.choice(len(heads), size=full_heads_max, replace=False)
         heads = [heads[i] for i in sorted(set(pick.tolist()) | {0, len(heads) - 1})]
     stats = []
+    lse_err = 0.0
     for b, h in heads:
         rows = np.arange(wl.N) if wl.N <= 2048 else _sample_rows(wl.N, rng, n=48)
         Or, Lr = oracle.attention_forward_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h],
                                                wl.scale, causal, rows)
         stats.append(check_o(o64[b, h, rows], Or, f"O[{b},{h}]", strict=q_mult == 1.0))
-        check_lse(l64[b, h, rows], Lr, f"LSE[{b},{h}]")
+        lse_err = max(lse_err, check_lse(l64[b, h, rows], Lr, f"LSE[{b},{h}]"))
     # every head, every row: finite, and LSE >= max visible score is implied
     # by LSE >= ln(1) + ... ; check the cheap bound LSE > -inf and O within
     # the convex hull of V columns
@@ -234,7 +235,7 @@ def _fwd_workload(name, causal, q_mult, full_heads_max, splits=None):
     lo = v.min(axis=2, keepdims=True) - 1e-2
     hi = v.max(axis=2, keepdims=True) + 1e-2
     assert np.all(o64 >= lo - np.abs(lo) * 2**-8) and np.all(o64 <= hi + np.abs(hi) * 2**-8)
-    _say(f"  max |dO| {max(s['max_abs_err'] for s in stats):.3e}; "
+    _say(f"  max |dO| {max(s['max_abs_err'] for s in stats):.3e}; max |dLSE| {lse_err:.3e}; "
          f"ulp allowance used {sum(s['needed_ulp_allowance'] for s in stats)}")
 
 
