@@ -197,25 +197,20 @@ def splitkv_measure(fa, make_inputs, splits: int, iters: int = 20) -> list:
 FP8_SHAPES = [(4, 16, 4096, 128, True, 5100), (1, 16, 16384, 128, True, 4100)]
 
 
-def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
+def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 50) -> list:
     """FP8 forward next to the bf16 forward on the same shapes, timed with
-    HIP events on the current stream (average over `iters` launches)."""
+    HIP events on the current stream: the median of `iters` launches after
+    the warm-up of ``_event_times`` (the inputs are encoded on the host
+    first, which leaves the GPU idle for seconds; 20 untimed launches alone
+    read the FP8 forward on C5's shape 12% slow)."""
     import numpy as np
     import torch
     out = []
     stream = torch.cuda.current_stream()
 
     def avg(fn):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(iters):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+        t = _event_times(fn, iters, 20)
+        return t[len(t) // 2]
 
     for B, H, N, d, causal, seed in FP8_SHAPES:
         x8 = make_inputs_fp8(B, H, N, d, seed=seed)
@@ -263,12 +258,23 @@ def fp8_measure(fa, make_inputs, make_inputs_fp8, iters: int = 20) -> list:
     return out
 
 
-def _event_times(fn, iters: int, warmup: int) -> list:
-    """Per-launch times (ms) of ``fn`` from HIP events on the current stream."""
+def _event_times(fn, iters: int, warmup: int, warm_s: float = 0.25) -> list:
+    """Per-launch times (ms) of ``fn`` from HIP events on the current stream,
+    after at least ``warmup`` untimed launches and ``warm_s`` seconds of them:
+    the timed legs follow host-side work (input encoding, the oracle's
+    samples) that leaves the GPU idle, and its clock takes a few hundred
+    milliseconds of load to settle."""
+    import time
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
     torch.cuda.synchronize()

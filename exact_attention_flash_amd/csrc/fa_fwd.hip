@@ -355,14 +355,18 @@ struct FwdWave {
     if (g == 0) a.lse[(int64_t)bh_ * N + row] = (m + log2_fast(l)) * kLn2;
   }
 
-  // One period (two barrier-separated slots) of a wave of group GRP.  R = t
-  // mod 3 names the buffers: K tile t in K buffer R, V tile t - 1 in V buffer
-  // (R + 2) mod 3.  The period also starts the copies of K tile t + 2 (into
-  // the buffer of K tile t - 1) and V tile t + 1 (into the buffer of V tile
-  // t - 2), both last read in the previous period, and ends once K tile t + 1
-  // and V tile t are in LDS for the next one.  Group 0 runs the matrix phase
-  // of tile t in the first slot and its softmax phase in the second; group 1
-  // runs the softmax phase of tile t - 1 and then the matrix phase of tile t.
+  // One period (two slots) of a wave of group GRP.  R = t mod 3 names the
+  // buffers: K tile t in K buffer R, V tile t - 1 in V buffer (R + 2) mod 3.
+  // The period also starts the copies of K tile t + 2 (into the buffer of K
+  // tile t - 1) and V tile t + 1 (into the buffer of V tile t - 2), both last
+  // read in the previous period, and ends at a workgroup barrier once K tile
+  // t + 1 and V tile t are in LDS for the next one.  Group 0 runs the matrix
+  // phase of tile t in the first slot and its softmax phase in the second;
+  // group 1 runs the softmax phase of tile t - 1 and then the matrix phase of
+  // tile t.  No barrier separates the slots: nothing read in one slot is
+  // written in the other, and the two groups' phases are of similar length,
+  // so they stay in step on their own (a barrier between the slots cost 1-2%;
+  // the FP8 forward, whose softmax phase is the longer one, keeps it).
   template <int R, int GRP>
   __device__ __forceinline__ void period(int t) {
     constexpr int KB = R, VB = (R + 2) % 3, KN = (R + 2) % 3, VN = (R + 1) % 3;
@@ -376,7 +380,6 @@ struct FwdWave {
       if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);
       softmax_phase(t - 1);
     }
-    block_barrier();
     if (GRP == 0) {
       if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, Nk, w, lane);
       if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);

@@ -294,7 +294,10 @@ struct Fp8Wave {
   }
 
   // One period of the ping-pong schedule; see the bf16 forward for the
-  // buffer rotation.
+  // buffer rotation.  Unlike there, a barrier separates the two slots: the
+  // softmax phase is the longer one here, and without the barrier the two
+  // groups' softmax phases overlap on the SIMD's vector unit (5% slower on
+  // causal B=4 H=16 N=4096 d=128).
   template <int R, int GRP>
   __device__ __forceinline__ void period(int t) {
     constexpr int KB = R, VB = (R + 2) % 3, KN = (R + 2) % 3, VN = (R + 1) % 3;
