@@ -643,8 +643,9 @@ struct QBlock {
   // the wave goes on issuing vector instructions): block 1's S and dP beside
   // block 0's softmax, the dQ products of block 0's chunks beside block 1's.
   // MASK: the tile straddles the diagonal or the end of the sequence.
+  // cj: the tile whose copies this one issues into the other stage, or -1.
   template <int ST, bool MASK>
-  __device__ __forceinline__ void tile(int j) {
+  __device__ __forceinline__ void tile(int j, int cj) {
     static_assert(BC == 64, "two 32-key blocks per tile");
     const int k0 = j * BC;
     const RowLane<D> rk = rowk.fresh();
@@ -654,6 +655,10 @@ struct QBlock {
     // scheduling regions; the compiler interleaves within each
     scores<ST>(0, s, dp, rk);
     __builtin_amdgcn_sched_barrier(0);
+    // the next tile's copies (cj < 0: none) go out here rather than before
+    // the first products: issued beside them they slowed the first block's
+    // score MFMAs (C5 query-block pass 0.404 -> 0.395 ms)
+    if (cj >= 0) issue<ST ^ 1>(cj);
     scores<ST>(1, s, dp, rk);
     softmax_ds<MASK>(0, k0, s, dp, dsb);
     __builtin_amdgcn_sched_barrier(0);
@@ -665,12 +670,14 @@ struct QBlock {
 
   template <int ST>
   __device__ __forceinline__ void step(int j) {
-    if (j + 1 < nt) issue<ST ^ 1>(j + 1);
     const int k0 = j * BC;
+    const int cj = j + 1 < nt ? j + 1 : -1;
     if (!(CAUSAL && (k0 > qw0 + C::QW - 1))) {
       const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > qw0));
-      if (need_mask) tile<ST, true>(j);
-      else tile<ST, false>(j);
+      if (need_mask) tile<ST, true>(j, cj);
+      else tile<ST, false>(j, cj);
+    } else if (cj >= 0) {
+      issue<ST ^ 1>(cj);
     }
     wait_vmem();
     __syncthreads();
