@@ -38,7 +38,8 @@
 //    the transposing LDS read (ds_read_b64_tr_b16);
 //  * exponentials are base 2 with log2(e) folded into the scale; the running
 //    max (and with it O and l) is moved only on tiles that raise some row's
-//    max, a branch the whole wave takes or skips;
+//    max by more than 2^8 (kLazyThreshold), a branch the whole wave takes or
+//    skips;
 //  * causal: key tiles past the block's last query are never loaded, tiles
 //    past a wave's last query are skipped by that wave, and only tiles that
 //    straddle the diagonal (or the ragged end of the sequence) are masked.
@@ -61,14 +62,22 @@ struct FwdCfg {
 };
 
 // Largest growth of the probabilities (in log2 units) tolerated before the
-// running max is moved.  Zero: the max moves whenever a tile raises it, so
-// the largest probability of every row is exactly 1 when it is rounded to
-// bf16 for the P V product.  With a stale max (a threshold of 8 was used
-// before) the dominant probability of a nearly one-hot row is some 2^x,
-// rounded with a relative error up to 2^-9, and that error lands on O
-// undivided: up to 0.018 on rows of large logits (Q x 8, |V| ~ 4), past the
-// 1e-2 bar.
-constexpr float kRescaleThreshold = 0.f;
+// running max is moved (and O and the row sums rescaled).
+//  * Lazy (the O and LSE outputs): 8, so probabilities stay below 2^8 and the
+//    max moves only when a tile raises some row of the wave by more than
+//    that; with N(0, 1) inputs that is the first tile of the row.  A stale
+//    max makes the dominant probability of a nearly one-hot row some 2^x,
+//    whose bf16 rounding (relative error up to 2^-9) would land on O
+//    undivided.  So the sum O is divided by also takes, for each tile, the
+//    rounding error of the tile's largest probability (the bf16 value the
+//    P V product used, minus the fp32 one): a one-hot row then gives its V
+//    row exactly, as with an exact max, at six vector operations per tile
+//    instead of 64 multiplies of O on most tiles.  LSE keeps the sum of the
+//    unrounded probabilities.
+//  * Eager (the split-KV partials, whose merge takes one row sum per range):
+//    0, the max moves whenever a tile raises it, so the dominant probability
+//    is exactly 1 when rounded.
+constexpr float kLazyThreshold = 8.f;
 
 // Per-lane source offsets of the asynchronous tile copies.  Copy t of a lane
 // fills 16-byte slot (t * NW + w) * 64 + lane of a tile: row r = slot / CPR,
@@ -137,10 +146,11 @@ struct FwdSmem {
   uint16_t* v[3];
 };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool LAZY>
 struct FwdWave {
   using C = FwdCfg<D>;
   static constexpr int BC = C::BC;
+  static constexpr float kThreshold = LAZY ? kLazyThreshold : 0.f;
 
   FwdSmem sm;
   DropArgs drop;  // dropout (DROP only)
@@ -154,6 +164,7 @@ struct FwdWave {
   float sl2;
   float m_run;   // running max of scale*log2(e)*s
   float l_part;  // this lane's share of the running row sum
+  float l_corr;  // LAZY: sum over tiles of bf16(p_max) - p_max (the same in both halves)
   bf16x8 qf[D / 16];
   f32x16 oacc[D / 32];  // O^T: lane holds O[qrow][32 db + 8(i/4) + 4g + i%4]
   f32x16 s[BC / 32];    // S^T of the tile between the matrix and softmax phases
@@ -236,21 +247,28 @@ struct FwdWave {
     for (int sb = 0; sb < BC / 32; ++sb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-    mx = max_halves(mx) * sl2;
+    const float mraw = max_halves(mx);  // the row's largest score in the tile (-inf if none)
+    mx = mraw * sl2;
     // Move the running max when this tile raises it for some query of the
     // wave (always on the first visible tile, where m = -inf).
-    if (__ballot(mx > m_run + kRescaleThreshold)) {
+    if (__ballot(mx > m_run + kThreshold)) {
       const float m_new = fmaxf(m_run, mx);
       // a query with every key so far masked keeps m = -inf and nothing to rescale
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
+      if constexpr (LAZY) l_corr *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    if constexpr (LAZY) {
+      // the tile's largest probability exactly as the loop below computes it
+      const float pt = exp2_fast(fmaf(mraw, sl2, -m_use));
+      l_corr += __uint_as_float(pack2(0.f, pt) & 0xffff0000u) - pt;
+    }
     // Dropout bytes of this lane's keys 16 n + 8 g + 0..7 (chunk n): the
     // lane computes the Philox call of 16-key group n = 2 m + g and swaps
     // half of it with the other wave half, which computed group 2 m + 1 - g.
@@ -280,7 +298,7 @@ struct FwdWave {
         p[jj] = exp2_fast(fmaf(s[kc2 >> 1][(kc2 & 1) * 8 + jj], sl2, -m_use));
         rs += p[jj];
       }
-      // the row sum takes every probability; the product with V only the kept ones
+      // the row sums take every probability; the product with V only the kept ones
       if constexpr (DROP) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
@@ -314,6 +332,7 @@ struct FwdWave {
     if (qw0 >= N) ntw = 0;  // no real query in this wave: copies and barriers only
     m_run = -INFINITY;
     l_part = 0.f;
+    l_corr = 0.f;
   }
 
   // K tiles 0 and 1 and V tile 0 of the item's range, before its first
@@ -331,17 +350,21 @@ struct FwdWave {
                         : zero_bf16x8();
   }
 
+  // The row sum O is divided by: l with the rounding corrections (LAZY).
+  __device__ __forceinline__ float lazy_sum(float l) const { return LAZY ? l + l_corr : l; }
+
   __device__ __forceinline__ void zero_o() {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
   }
 
   // Epilogue of the item with head bh_ whose lane row is row: one division
-  // by l (and the dropout rescale), LSE = (m + log2 l) ln 2.
+  // by lo, the row sum O is normalised with (and the dropout rescale),
+  // LSE = (m + log2 l) ln 2.
   __device__ __forceinline__ void store_out(const FwdArgs& a, int bh_, int row, float l,
-                                            float m) const {
+                                            float lo, float m) const {
     if (row >= N) return;
-    const float inv = DROP ? drop.scale / l : 1.f / l;
+    const float inv = DROP ? drop.scale / lo : 1.f / lo;
     uint16_t* Orow = a.o + (int64_t)bh_ * N * D + (int64_t)row * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -428,7 +451,7 @@ fa_fwd_kernel(FwdArgs a) {
   const int nqb = (N + C::BR - 1) / C::BR;
 
   // per-lane constants, the same for every item
-  FwdWave<D, CAUSAL, DROP> f;
+  FwdWave<D, CAUSAL, DROP, !SPLIT> f;
   f.sm = FwdSmem{{k0s, k1s, k2s}, {v0s, v1s, v2s}};
   f.drop = a.drop;
   f.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -511,6 +534,7 @@ fa_fwd_kernel(FwdArgs a) {
       if (f.grp == 0) f.template run<0>();
       else f.template run<1>();
       const float l = sum_halves(f.l_part);
+      const float lo = f.lazy_sum(l);
       const float m = f.m_run;
       const int cur_bh = f.bh, cur_row = f.qrow;
       const int L = walk.item(r);
@@ -519,7 +543,7 @@ fa_fwd_kernel(FwdArgs a) {
         f.begin_item(a, bh, CAUSAL ? nqb - 1 - qb : qb, 0, 1);
         f.issue_prologue(a);
       }
-      f.store_out(a, cur_bh, cur_row, l, m);
+      f.store_out(a, cur_bh, cur_row, l, lo, m);
       if (L < 0) break;
       f.zero_o();
       // the previous item's scores and probabilities are dead: say so
