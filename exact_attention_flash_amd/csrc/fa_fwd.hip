@@ -394,20 +394,29 @@ struct FwdWave {
   __device__ __forceinline__ void period(int t) {
     constexpr int KB = R, VB = (R + 2) % 3, KN = (R + 2) % 3, VN = (R + 1) % 3;
     const bool kn = t + 2 < nt, vn = t + 1 < nt;
-    // each wave starts its share of the copies in its softmax slot, off the
-    // matrix phase's critical path
+    // Each wave starts its share of the copies in the slot that has room for
+    // them: the softmax slot without dropout (off the matrix phase's critical
+    // path), the matrix slot with dropout, whose softmax slot (with its Philox
+    // draws) is the longer one.  Measured on C5: 0.275 against 0.290 ms
+    // without dropout, 0.384 against 0.393 with it.
+    constexpr bool CP_M = DROP;
+    // this wave's share of the copies of K tile t + 2 and V tile t + 1
+    auto copies = [&](int t_, bool kn_, bool vn_) {
+      if (kn_) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t_ + 2) * BC, Nk, w, lane);
+      if (vn_) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t_ + 1) * BC, Nk, w, lane);
+    };
     if (GRP == 0) {
+      if (CP_M) copies(t, kn, vn);
       matrix_phase<KB, VB>(t);
     } else {
-      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, Nk, w, lane);
-      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);
+      if (!CP_M) copies(t, kn, vn);
       softmax_phase(t - 1);
     }
     if (GRP == 0) {
-      if (kn) cp.template issue<true, DROP>(Kh, sm.k[KN], (t0 + t + 2) * BC, Nk, w, lane);
-      if (vn) cp.template issue<false, DROP>(Vh, sm.v[VN], (t0 + t + 1) * BC, Nk, w, lane);
+      if (!CP_M) copies(t, kn, vn);
       softmax_phase(t);
     } else {
+      if (CP_M) copies(t, kn, vn);
       matrix_phase<KB, VB>(t);
     }
     if (kn) wait_vmem_except_last<2 * C::COPIES>();
