@@ -380,6 +380,52 @@ def test_long_sequence_fwd_bwd(B, H, N, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_fwd_stale_max_rounding(d):
+    """The forward moves its running max only when a tile raises it by more
+    than 2^8 (in log2 units), so a later tile's largest probability can be
+    some 2^x > 1 whose bf16 rounding feeds the P V product.  Here every query
+    sees key A (score 0, tile 0), key B in tile 3 with probability 2^x in
+    [128.3, 128.45] relative to A (rounded to 128 in bf16, 0.3% low), and 254
+    keys at score -100; every V row is the same vector v, so the exact O is v
+    whatever the weights.  Dividing by the unrounded row sum would put O 0.3%
+    low, one bf16 ulp off in every element; with each tile's rounding
+    correction in the divisor O comes out as v exactly."""
+    from exact_attention_flash_amd.inputs import f32_to_bf16_bits
+    _say(f"stale-max rounding d={d}")
+    B, H, N = 1, 2, 256
+    scale = default_scale(d)
+    sl2 = np.float32(scale) * np.float32(1.4426950408889634)
+    # key B's score: 4 a + b for bf16 a, b, chosen so that 2^(s sl2) rounds down by ~0.3%
+    best = None
+    for a in (f32_to_bf16_bits(np.float32(x)) for x in np.arange(8.0, 16.0, 0.0625)):
+        af = float(oracle.widen_bf16(np.asarray(a).reshape(1))[0])
+        for bb in f32_to_bf16_bits(np.linspace(0.0, 0.5, 257).astype(np.float32)):
+            bf = float(oracle.widen_bf16(np.asarray(bb).reshape(1))[0])
+            xs = np.float32(np.float32(4.0 * af + bf) * sl2)
+            if 128.3 <= 2.0 ** float(xs) <= 128.45:
+                best = (af, bf)
+                break
+        if best:
+            break
+    assert best is not None
+    q = np.zeros((B, H, N, d), np.float32)
+    q[..., 0], q[..., 1] = 4.0, 1.0
+    k = np.zeros((B, H, N, d), np.float32)
+    k[..., 0] = -25.0                  # score -100 for every other key
+    k[:, :, 5, 0] = 0.0                # key A, tile 0: score 0
+    k[:, :, 200, 0], k[:, :, 200, 1] = best   # key B, tile 3
+    v_row = (1.875 * 2.0 ** (np.arange(d) % 4 - 2) * (-1.0) ** np.arange(d)).astype(np.float32)
+    v = np.broadcast_to(v_row, (B, H, N, d)).copy()
+    x = {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
+    (_, _, _), o, lse = _run_fwd(x, False, scale)
+    o64 = bf16_to_f64(o)
+    err = np.abs(o64 - v_row.astype(np.float64)).max()
+    assert err == 0.0, f"O off v by {err:.3e} (the divisor lacks the bf16 rounding of p_max)"
+    _, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, False)
+    check_lse(lse.cpu().numpy().astype(np.float64), L_ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("pattern", ["rising", "falling", "large"])
 def test_fwd_extreme_logits(d, causal, pattern):
