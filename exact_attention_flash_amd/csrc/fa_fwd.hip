@@ -17,7 +17,7 @@
 //    matrix phase (S^T = K Q^T for tile t and O^T += V^T P^T for tile t - 1,
 //    all MFMA and LDS reads) with a softmax phase (mask, row max, exp2, row
 //    sum, bf16 packing: all VALU) for tile t.  Waves 0-3 and 4-7 run these
-//    phases half a period apart, separated by workgroup barriers, so on each
+//    phases half a period apart, with one workgroup barrier per period, so on each
 //    SIMD one wave keeps the matrix core busy while the other does the
 //    softmax arithmetic.  Measured on gfx950, an MFMA-only wave and a
 //    VALU-only wave on one SIMD overlap almost completely; two waves that
@@ -67,7 +67,7 @@ struct FwdCfg {
 //    max moves only when a tile raises some row of the wave by more than
 //    that; with N(0, 1) inputs that is the first tile of the row.  A stale
 //    max makes the dominant probability of a nearly one-hot row some 2^x,
-//    whose bf16 rounding (relative error up to 2^-9) would land on O
+//    whose bf16 rounding (relative error up to 2^-8) would land on O
 //    undivided.  So the sum O is divided by also takes, for each tile, the
 //    rounding error of the tile's largest probability (the bf16 value the
 //    P V product used, minus the fp32 one): a one-hot row then gives its V
